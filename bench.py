@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged-KV decode step on one MI355X.
+
+A step is the whole hot path for one decode layer: slot resolution for the new
+tokens, the scatter-write of their K/V into the paged cache, and decode attention
+(plus the log-sum-exp merge when the context is split).  Inputs are synthetic and
+seeded, resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout:
+  value        effective KV GB/s of the step = algorithmic bytes of a step / step time
+  roofline     the decode call (its dominant kernel) against the 8 TB/s HBM peak,
+               timed with HIP events on its own stream, L2/MALL flushed before each rep
+  cpu_baseline the fp64 oracle timed on this host's cores on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective KV GB/s (% of HBM peak) and seq-heads/s per decode layer"
+DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+KERNEL_SOURCES = ["paged_kv_cache_27_amd/csrc/decode.hip", "paged_kv_cache_27_amd/csrc/pkv_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama3-8b-shaped-bf16-64seq",
+                    help="workload name or 1-based index (default: the 8B-shaped layer)")
+    ap.add_argument("--reps", type=int, default=30, help="cold-cache reps of the roofline leg")
+    ap.add_argument("--all", action="store_true", help="also measure every other workload (stderr + --json-out)")
+    ap.add_argument("--json-out", default=None, help="write per-workload results here")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the oracle leg")
+    ap.add_argument("--partition", type=int, default=None, help="override the partition size")
+    return ap.parse_args()
+
+
+def pick_config(spec):
+    from workloads import CONFIGS
+    if str(spec).isdigit():
+        return CONFIGS[int(spec) - 1]
+    for c in CONFIGS:
+        if c.name == spec:
+            return c
+    raise SystemExit(f"unknown workload {spec}; known: {[c.name for c in CONFIGS]}")
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move: decode reads each sequence's whole context once per KV
+    head plus q, out, its block-table entries and context length; the write reads the new
+    K/V and the slots and writes the cache rows; slot resolution reads ids/positions/table
+    entries and writes slots."""
+    c = w.cfg
+    n, hq, hkv, d, B = c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size
+    ctx = w.context_lens.astype("int64")
+    kv = int(ctx.sum()) * hkv * d * 2 * DT_BYTES[c.kv_dtype]
+    table = int(((ctx + B - 1) // B).sum()) * 4 + 4 * n
+    qo = n * hq * d * (DT_BYTES[c.q_dtype] + DT_BYTES[c.out_dtype])
+    decode = kv + table + qo
+    write = n * hkv * d * 2 * (DT_BYTES[c.src_dtype] + DT_BYTES[c.kv_dtype]) + 8 * n
+    slots = n * (4 + 4 + 4 + 8)
+    unique_kv = w.kv_bytes_unique()
+    return {"decode": decode, "kv": kv, "kv_unique": unique_kv, "write": write, "slots": slots,
+            "step": decode + write + slots}
+
+
+class Step:
+    """Device-resident inputs of one decode step and the three ABI calls that run it."""
+
+    def __init__(self, w, partition=None):
+        import numpy as np
+        import torch
+        import paged_kv_cache_27_amd as pkv
+        from workloads import POISON_BITS, cache_shape
+
+        self.pkv, self.torch, self.w = pkv, torch, w
+        c = w.cfg
+        dev = "cuda"
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+        def up(x, dt):
+            if dt == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+        bits = POISON_BITS[c.kv_dtype]
+        store = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "fp8": torch.uint8}[c.kv_dtype]
+        view = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}[c.kv_dtype]
+        self.k_cache = torch.full(cache_shape(w), bits, dtype=store, device=dev).view(view)
+        self.v_cache = torch.full(cache_shape(w), bits, dtype=store, device=dev).view(view)
+        self.kv_dtype = "fp8" if c.kv_dtype == "fp8" else None
+        self.block_tables = torch.from_numpy(w.block_tables).to(dev)
+        self.context_lens = torch.from_numpy(w.context_lens).to(dev)
+        self.q = up(w.q, c.q_dtype)
+        self.new_k = up(w.new_k, c.src_dtype)
+        self.new_v = up(w.new_v, c.src_dtype)
+        self.new_seq = torch.from_numpy(w.new_seq).to(dev)
+        self.new_pos = torch.from_numpy(w.new_pos).to(dev)
+        self.slots = torch.empty(c.num_seqs, dtype=torch.int64, device=dev)
+        self.out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=tdt[c.out_dtype], device=dev)
+        self.partition = c.partition_size if partition is None else partition
+        need = pkv.paged_attention_workspace_size(c.num_seqs, c.num_q_heads, c.head_dim,
+                                                  w.max_context_len, c.block_size, self.partition)
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        # history: every cached token written once through the same write kernel
+        if w.hist_seq.size:
+            hs = torch.from_numpy(w.hist_seq).to(dev)
+            hp = torch.from_numpy(w.hist_pos).to(dev)
+            hslots = pkv.paged_kv_slot_mapping(hs, hp, self.block_tables, c.block_size)
+            hk, hv = up(w.hist_k, c.src_dtype), up(w.hist_v, c.src_dtype)
+            pkv.paged_kv_write(hslots, hk, hv, self.k_cache, self.v_cache, self.kv_dtype,
+                               w.k_scale, w.v_scale)
+            torch.cuda.synchronize()
+            del hk, hv, hs, hp, hslots
+
+    def slot_map(self):
+        self.pkv.paged_kv_slot_mapping(self.new_seq, self.new_pos, self.block_tables,
+                                       self.w.cfg.block_size, slot_mapping=self.slots)
+
+    def write(self):
+        w = self.w
+        self.pkv.paged_kv_write(self.slots, self.new_k, self.new_v, self.k_cache, self.v_cache,
+                                self.kv_dtype, w.k_scale, w.v_scale)
+
+    def decode(self):
+        w = self.w
+        self.pkv.paged_attention_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
+                                        self.context_lens, w.scale, self.out, w.max_context_len,
+                                        partition_size=self.partition, workspace=self.workspace,
+                                        kv_dtype=self.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+
+    def step(self):
+        self.slot_map()
+        self.write()
+        self.decode()
+
+
+def traffic_for(cfg_name):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    f = ROOT / "profiles" / "traffic.json"
+    if not f.exists():
+        return None
+    data = json.loads(f.read_text())
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES:
+        h.update((ROOT / src).read_bytes())
+    entry = data.get(cfg_name)
+    if not entry or entry.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    return entry.get("bytes_per_call")
+
+
+def measure(cfg, args, partition=None):
+    import numpy as np
+    import torch
+    from workloads import make_workload
+
+    t0 = time.time()
+    w = make_workload(cfg)
+    log(f"[{cfg.name}] inputs generated in {time.time() - t0:.1f}s")
+    st = Step(w, partition if partition is not None else args.partition)
+    nbytes = algorithmic_bytes(w)
+
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        st.step()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    ms_step = (t2 - t1) * 1e3 / args.steps
+
+    # Cold-cache leg: L2 and MALL flushed before each rep; HIP events on the stream the
+    # library launches on (torch's current stream, which the binding passes down).
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.reps)]
+    for r in range(args.reps):
+        flush.random_(0, 255) if r == 0 else flush.add_(1)
+        e = ev[r]
+        e[0].record()
+        st.slot_map()
+        e[1].record()
+        st.write()
+        e[2].record()
+        st.decode()
+        e[3].record()
+    torch.cuda.synchronize()
+    t_slot = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_write = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    t_dec = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    del flush
+    dec_ms = float(np.mean(t_dec))
+    achieved = nbytes["decode"] / (dec_ms * 1e-3) / 1e9
+    part = st.partition
+    if part == 0:
+        part = st.pkv.paged_attention_auto_partition(cfg.num_seqs, cfg.num_kv_heads,
+                                                     w.max_context_len, cfg.block_size)
+    res = {
+        "workload": cfg.name, "ms_per_step": ms_step,
+        "step_GBps": nbytes["step"] / (ms_step * 1e-3) / 1e9,
+        "seq_heads_per_s": cfg.num_seqs * cfg.num_q_heads / (ms_step * 1e-3),
+        "decode_ms_cold_mean": dec_ms, "decode_ms_cold_median": float(np.median(t_dec)),
+        "decode_ms_cold_p10": float(np.percentile(t_dec, 10)),
+        "decode_ms_cold_p90": float(np.percentile(t_dec, 90)),
+        "write_ms_cold_mean": float(np.mean(t_write)), "slotmap_ms_cold_mean": float(np.mean(t_slot)),
+        "decode_GBps_cold": achieved, "decode_frac_hbm_peak": achieved / HBM_PEAK_GBS,
+        "decode_unique_GBps_cold": (nbytes["decode"] - nbytes["kv"] + nbytes["kv_unique"]) / (dec_ms * 1e-3) / 1e9,
+        "bytes": nbytes, "partition": int(part) if part and part > 0 else "single-pass",
+        "max_context_len": w.max_context_len, "sum_context": int(w.context_lens.sum()),
+    }
+    log(f"[{cfg.name}] step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s), decode cold "
+        f"{dec_ms * 1e3:.1f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak), "
+        f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, partition {res['partition']}")
+    return w, st, res
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle on this host's cores over whole sequences (all query heads), taken
+    in order until the wall budget is spent."""
+    import numpy as np
+    from oracle.oracle import Oracle
+    from workloads import poisoned_cache
+
+    orc = Oracle()
+    c = w.cfg
+    kc, vc = poisoned_cache(w), poisoned_cache(w)
+    hs = orc.slot_mapping(w.hist_seq, w.hist_pos, w.block_tables, c.block_size)
+    orc.kv_write(hs, w.hist_k, w.hist_v, c.src_dtype, kc, vc, c.kv_dtype, w.k_scale, w.v_scale)
+    ns = orc.slot_mapping(w.new_seq, w.new_pos, w.block_tables, c.block_size)
+    orc.kv_write(ns, w.new_k, w.new_v, c.src_dtype, kc, vc, c.kv_dtype, w.k_scale, w.v_scale)
+    threads = min(16, len(os.sched_getaffinity(0)))
+    done_seqs, elapsed, tokens = 0, 0.0, 0
+    per = max(1, threads // 2)
+    while done_seqs < c.num_seqs and elapsed < budget_s:
+        seqs = range(done_seqs, min(c.num_seqs, done_seqs + per))
+        pairs = np.array([(s, h) for s in seqs for h in range(c.num_q_heads)], np.int32)
+        t0 = time.perf_counter()
+        orc.decode(w.q, c.q_dtype, kc, vc, c.kv_dtype, w.block_tables, w.context_lens, w.scale,
+                   w.k_scale, w.v_scale, pairs=pairs, threads=threads)
+        elapsed += time.perf_counter() - t0
+        tokens += int(w.context_lens[list(seqs)].sum())
+        done_seqs = seqs[-1] + 1
+    kv_bytes = tokens * c.num_kv_heads * c.head_dim * 2 * DT_BYTES[c.kv_dtype]
+    return {"value": kv_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seq_heads_per_s": done_seqs * c.num_q_heads / elapsed,
+            "sample": f"decode of sequences 0..{done_seqs - 1} of {c.num_seqs} (all {c.num_q_heads} "
+                      f"query heads, {tokens} context tokens), fp64, {elapsed:.1f}s wall on {threads} threads"}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this path has "
+              "no multi-GPU leg; sharding is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_27_amd as pkv
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    pkv.load_library()  # raises if the HIP library is missing: there is no fallback
+    cfg = pick_config(args.config)
+    w, st, res = measure(cfg, args)
+    del st
+    torch.cuda.empty_cache()
+    others = []
+    if args.all:
+        from workloads import CONFIGS
+        for c in CONFIGS:
+            if c.name != cfg.name:
+                _, s2, r2 = measure(c, args)
+                others.append(r2)
+                del s2
+                torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"[cpu oracle] {cpu['value']:.3f} GB/s on {cpu['cores']} threads: {cpu['sample']}")
+    traffic = traffic_for(cfg.name)
+    c = cfg
+    line = {
+        "metric": METRIC, "value": round(res["step_GBps"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c.kv_dtype, "data": "synthetic",
+        "config": {"workload": c.name, "num_seqs": c.num_seqs, "num_q_heads": c.num_q_heads,
+                   "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+                   "block_size": c.block_size, "q_dtype": c.q_dtype, "kv_dtype": c.kv_dtype,
+                   "context_lens": f"{c.ctx_kind}{tuple(c.ctx_params)}",
+                   "sum_context": res["sum_context"], "partition": res["partition"],
+                   "seed": c.seed},
+        "pct_hbm_peak": round(100 * res["step_GBps"] / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(res["seq_heads_per_s"], 1),
+        "roofline": {"bound": "hbm", "achieved": round(res["decode_GBps_cold"], 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(res["decode_frac_hbm_peak"], 4), "traffic": traffic,
+                     "kernel": "paged_attention_decode call (decode_kernel + merge_kernel)",
+                     "bytes_per_launch": res["bytes"]["decode"],
+                     "mean_launch_ms": round(res["decode_ms_cold_mean"], 6)},
+        "cpu_baseline": cpu,
+    }
+    if args.json_out:
+        Path(args.json_out).parent.mkdir(parents=True, exist_ok=True)
+        Path(args.json_out).write_text(json.dumps({"headline": res, "others": others, "cpu": cpu}, indent=1))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV cache decode path for AMD MI355X (gfx950).
+ *
+ * One decode step of one attention layer:
+ *   1. paged_kv_slot_mapping  -- resolve (sequence, position) to a cache slot
+ *                                through the block table;
+ *   2. paged_kv_write         -- store each new token's K and V in its slot;
+ *   3. paged_attention_decode -- every query head of the new token attends over
+ *                                its sequence's whole cached context, new token
+ *                                included, reading K/V through the block table.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller (allocated by
+ *     any HIP allocator, e.g. PyTorch).  The library allocates and frees nothing
+ *     and keeps no global mutable state; concurrent calls on different streams
+ *     are safe as long as they do not write the same memory.
+ *   - Every call is asynchronous on `stream` (NULL = the null stream).  Buffers
+ *     must stay alive until the caller synchronises.  Host-visible argument
+ *     errors are returned before anything is launched; no call synchronises
+ *     with the device, so errors inside kernels surface at the caller's next sync.
+ *   - Return value: PKV_OK (0) or a negative pkv_status.  No exception crosses
+ *     the ABI.  pkv_status_string() names each code.
+ *
+ * Cache layout (both K and V): [num_blocks][num_kv_heads][block_size][head_dim],
+ * row-major.  One (block, KV head) tile is block_size * head_dim contiguous
+ * elements, so a 16-token bf16 tile of head_dim 128 is 4 KiB read with 16-byte
+ * loads per lane.  Token position p of sequence s lives at physical block
+ * block_tables[s][p / block_size], offset p % block_size ("PagedAttention por
+ * dentro...", section "La tabla de paginas (block table)"; "Optimizacion de
+ * Inferencia LLM", section "PagedAttention: Conceptos de SO...", get_physical_block).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3 /* OCP e4m3fn: bias 7, no infinities, S.1111.111 = NaN, max 448 */
+} pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_DTYPE = -2,       /* unsupported dtype or dtype combination */
+  PKV_ERR_SHAPE = -3,       /* unsupported head_dim / block_size / group size, or bad sizes */
+  PKV_ERR_HEADS = -4,       /* num_q_heads is not a multiple of num_kv_heads */
+  PKV_ERR_WORKSPACE = -5,   /* workspace too small, or bad partition size */
+  PKV_ERR_LAUNCH = -6       /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/* Describes one layer's paged cache (K and V share it). */
+typedef struct {
+  int64_t num_blocks;   /* physical blocks in the pool */
+  int32_t block_size;   /* tokens per block: 16 or 32 */
+  int32_t num_kv_heads; /* H_kv */
+  int32_t head_dim;     /* d_h: 64 or 128 */
+  int32_t dtype;        /* pkv_dtype of the stored elements */
+  float k_scale;        /* fp8 only: stored code * k_scale = K value (1.0 otherwise) */
+  float v_scale;        /* fp8 only: stored code * v_scale = V value */
+} pkv_cache_desc;
+
+/*
+ * slot_mapping[t] = block_tables[seq_ids[t]][positions[t] / B] * B + positions[t] % B
+ * for each of num_tokens tokens; a negative position gives slot -1 ("skip").
+ * Source: "Optimizacion de Inferencia LLM", section "PagedAttention: Conceptos de
+ * SO...", BlockTable.get_physical_block.
+ *   seq_ids, positions : int32 [num_tokens]
+ *   block_tables       : int32 [num_seqs][max_blocks_per_seq]
+ *   slot_mapping       : int64 [num_tokens] (output)
+ * Preconditions (not checked on the device): seq_ids in range and
+ * positions[t] / B < max_blocks_per_seq.  num_tokens == 0 launches nothing.
+ */
+int paged_kv_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t block_size, int64_t* slot_mapping, hipStream_t stream);
+
+/*
+ * Store token t's K and V at cache[slot / B][h][slot % B][:] for every KV head h.
+ * Source: "PagedAttention por dentro...", section "La tabla de paginas (block
+ * table)" (a new token fills the last block's free slot or the first slot of a
+ * freshly appended block); "Capitulo 2", section "Que guarda realmente el KV
+ * cache" (the new k_t, v_t join the cached state).
+ *   slot_mapping : int64 [num_tokens]; a negative slot skips that token
+ *   k, v         : [num_tokens][num_kv_heads][head_dim] of src_dtype (f32/f16/bf16)
+ *   k_cache, v_cache : the cache described by `cache`
+ * Conversion: same dtype -> bit copy; fp8 cache -> e4m3fn of fl32(fl32(x) / scale)
+ * rounded to nearest-even, saturated to +-448, NaN kept NaN.
+ * Preconditions (not checked on the device): slots unique and < num_blocks * B.
+ */
+int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* k,
+                   const void* v, pkv_dtype src_dtype, void* k_cache, void* v_cache,
+                   const pkv_cache_desc* cache, hipStream_t stream);
+
+/* Bytes of workspace paged_attention_decode needs for this shape (0 if the call
+ * runs in a single pass).  partition_size as for paged_attention_decode. */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_context_len, int32_t block_size,
+                                      int32_t partition_size);
+
+/*
+ * out[s][h][:] = softmax_t(scale * q[s][h] . K_t) V_t over t = 0 .. context_lens[s]-1,
+ * K_t, V_t of KV head h / (num_q_heads / num_kv_heads), read through block_tables.
+ * Sources: "Capitulo 2", section "Que guarda realmente el KV cache" (Attn(q_t,
+ * [K_{1:t-1}, k_t], [V_{1:t-1}, v_t])); "Optimizacion de Inferencia LLM", sections
+ * "El Cuello de Botella..." (softmax(q k^T / sqrt(d_head)) v) and "PagedAttention:
+ * Conceptos de SO..." (per-block loads with online-softmax accumulation); "La
+ * despensa por casilleros", section "El mecanismo" (gather in logical order).
+ *   q            : [num_seqs][num_q_heads][head_dim] of q_dtype
+ *   block_tables : int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(context_lens[s] / B) are never read
+ *   context_lens : int32 [num_seqs], counting the new token (already written)
+ *   max_context_len : host-side upper bound of context_lens (sizes the grid)
+ *   out          : [num_seqs][num_q_heads][head_dim] of out_dtype (f32/f16/bf16)
+ *   partition_size : 0 = library's choice; -1 = one pass per (sequence, KV head);
+ *                    else tokens per partition, a positive multiple of block_size;
+ *                    partial results are merged by a log-sum-exp pass
+ *   workspace    : device scratch of >= paged_attention_workspace_size() bytes
+ *                  (may be NULL when that size is 0)
+ * Supported: head_dim 64 or 128; block_size 16 or 32; group size
+ * num_q_heads / num_kv_heads in 1..16; (q, cache) dtypes (f32, f32), (f16, f16),
+ * (bf16, bf16), (bf16 or f16, fp8).  Accumulation is fp32; the output is rounded
+ * to nearest-even.  context_lens[s] == 0 gives zeros.
+ * Preconditions (not checked on the device): 0 <= context_lens[s] <=
+ * max_context_len; block IDs in [0, num_blocks) for the entries read.
+ */
+int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
+                           int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                           const pkv_cache_desc* cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, float scale, void* out,
+                           pkv_dtype out_dtype, int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Partition size (tokens) paged_attention_decode uses for partition_size == 0,
+ * or 0 if it runs a single pass. */
+int32_t paged_attention_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t block_size);
+
+/* Static description of a status code. */
+const char* pkv_status_string(int status);
+
+/* ABI version: bumps when any signature or layout above changes. */
+int32_t pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,192 @@
+"""ctypes binding of libpagedkv.so: argument marshalling only.
+
+Every step of the decode path runs in the HIP library; this module turns torch
+tensors into device pointers, sizes and the current HIP stream, calls the C ABI
+(include/pagedkv.h) and raises on a non-zero status.  There is no fallback: a
+missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libpagedkv.so"
+
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+_TORCH_CODES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
+                torch.float8_e4m3fn: FP8_E4M3}
+_NAME_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8_E4M3}
+
+STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHAPE",
+          -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH"}
+
+EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_workspace_size",
+            "paged_attention_decode", "paged_attention_auto_partition", "pkv_status_string",
+            "pkv_abi_version"]
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of pkv_cache_desc."""
+    _fields_ = [("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({message})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) the HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = Path(path)
+    if not path.exists():
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_27_amd.build`")
+    lib = ctypes.CDLL(str(path))
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.paged_kv_slot_mapping.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp]
+    lib.paged_kv_slot_mapping.restype = ctypes.c_int
+    lib.paged_kv_write.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp,
+                                   ctypes.POINTER(CacheDesc), vp]
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_workspace_size.restype = ctypes.c_size_t
+    lib.paged_attention_decode.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp,
+                                           ctypes.POINTER(CacheDesc), vp, i32, vp, i32, f32, vp,
+                                           ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
+    lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_auto_partition.argtypes = [i32, i32, i32, i32]
+    lib.paged_attention_auto_partition.restype = i32
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_abi_version.argtypes = []
+    lib.pkv_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = load_library().pkv_status_string(status).decode()
+        raise PagedKVError(fn, status, msg)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors handed to the HIP library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors handed to the HIP library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def dtype_code(x) -> int:
+    if isinstance(x, str):
+        return _NAME_CODES[x]
+    if isinstance(x, torch.dtype):
+        return _TORCH_CODES[x]
+    return int(x)
+
+
+def cache_desc(k_cache: torch.Tensor, kv_dtype=None, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> CacheDesc:
+    """Descriptor of a [num_blocks][H_kv][B][d_h] cache tensor.  An fp8 cache may be a
+    torch.float8_e4m3fn tensor or a uint8 tensor with kv_dtype='fp8'."""
+    nb, hkv, bs, d = k_cache.shape
+    code = dtype_code(kv_dtype if kv_dtype is not None else k_cache.dtype)
+    return CacheDesc(nb, bs, hkv, d, code, float(k_scale), float(v_scale))
+
+
+def pkv_status_string(status: int) -> str:
+    return load_library().pkv_status_string(status).decode()
+
+
+def pkv_abi_version() -> int:
+    return int(load_library().pkv_abi_version())
+
+
+def paged_kv_slot_mapping(seq_ids: torch.Tensor, positions: torch.Tensor,
+                          block_tables: torch.Tensor, block_size: int,
+                          slot_mapping: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    lib = load_library()
+    n = seq_ids.numel()
+    if slot_mapping is None:
+        slot_mapping = torch.empty(n, dtype=torch.int64, device=seq_ids.device)
+    assert seq_ids.dtype == torch.int32 and positions.dtype == torch.int32
+    assert block_tables.dtype == torch.int32 and slot_mapping.dtype == torch.int64
+    _check("paged_kv_slot_mapping",
+           lib.paged_kv_slot_mapping(_ptr(seq_ids), _ptr(positions), n, _ptr(block_tables),
+                                     block_tables.shape[1], block_size, _ptr(slot_mapping),
+                                     _stream(stream)))
+    return slot_mapping
+
+
+def paged_kv_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype=None,
+                   k_scale: float = 1.0, v_scale: float = 1.0, src_dtype=None,
+                   stream=None) -> None:
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
+    assert slot_mapping.dtype == torch.int64
+    src = dtype_code(src_dtype if src_dtype is not None else k.dtype)
+    _check("paged_kv_write",
+           lib.paged_kv_write(_ptr(slot_mapping), slot_mapping.numel(), _ptr(k), _ptr(v), src,
+                              _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def paged_attention_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
+                                   max_context_len: int, block_size: int,
+                                   partition_size: int = 0) -> int:
+    return int(load_library().paged_attention_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                             max_context_len, block_size,
+                                                             partition_size))
+
+
+def paged_attention_auto_partition(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                                   block_size: int) -> int:
+    return int(load_library().paged_attention_auto_partition(num_seqs, num_kv_heads,
+                                                             max_context_len, block_size))
+
+
+def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           scale: float, out: torch.Tensor, max_context_len: int,
+                           partition_size: int = 0, workspace: torch.Tensor | None = None,
+                           kv_dtype=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                           q_dtype=None, out_dtype=None, stream=None) -> torch.Tensor:
+    """Decode attention into `out`.  `workspace` (a byte tensor) is allocated here by torch
+    when the call needs one and none is given."""
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
+    n, hq, d = q.shape
+    need = paged_attention_workspace_size(n, hq, d, max_context_len, desc.block_size,
+                                          partition_size)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    _check("paged_attention_decode",
+           lib.paged_attention_decode(
+               _ptr(q), dtype_code(q_dtype if q_dtype is not None else q.dtype), n, hq,
+               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
+               block_tables.shape[1], _ptr(context_lens), int(max_context_len), float(scale),
+               _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
+               int(partition_size), _ptr(workspace) if need else None,
+               workspace.numel() if need else 0, _stream(stream)))
+    return out

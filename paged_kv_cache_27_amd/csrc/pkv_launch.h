@@ -1,0 +1,61 @@
+// Internal launcher interface between the C ABI layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct WriteArgs {
+  const int64_t* slot_mapping;
+  int32_t num_tokens;
+  const void* k;
+  const void* v;
+  int src_dtype;
+  void* k_cache;
+  void* v_cache;
+  int cache_dtype;
+  int32_t num_kv_heads, head_dim, block_size;
+  float k_scale, v_scale;
+};
+
+struct DecodeArgs {
+  const void* q;
+  int q_dtype;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
+  int cache_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  float k_scale, v_scale;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  float scale;
+  void* out;
+  int out_dtype;
+  int32_t partition;       // tokens per partition (> 0)
+  int32_t num_partitions;  // grid extent; 1 = single pass (no workspace)
+  float* ws_m;             // [N][H_q][P] running max (log2 domain), split mode only
+  float* ws_l;             // [N][H_q][P] softmax denominators
+  float* ws_acc;           // [N][H_q][P][D] unnormalised outputs
+};
+
+hipError_t launch_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t n,
+                               const int32_t* block_tables, int32_t max_blocks,
+                               int32_t block_size, int64_t* slots, hipStream_t stream);
+hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+// Returns hipErrorInvalidValue for an unsupported combination (checked earlier by the ABI).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Workspace layout for split mode, each array 256-byte aligned.
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t ws_ml_bytes(int64_t n, int64_t hq, int64_t parts) {
+  return align256((size_t)(n * hq * parts) * sizeof(float));
+}
+inline size_t ws_total_bytes(int64_t n, int64_t hq, int64_t d, int64_t parts) {
+  return 2 * ws_ml_bytes(n, hq, parts) + align256((size_t)(n * hq * parts * d) * sizeof(float));
+}
+
+}  // namespace pkv

@@ -1,0 +1,117 @@
+"""GPU side of the parity tests: run one decode step through the C ABI."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import paged_kv_cache_27_amd as pkv
+from workloads import POISON_BITS, cache_shape
+
+TOL = {"f32": 4e-3, "f16": 4e-3, "bf16": 4e-3, "fp8": 2e-2}
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def poisoned_device_cache(w, device="cuda") -> torch.Tensor:
+    dt = w.cfg.kv_dtype
+    bits = POISON_BITS[dt]
+    shape = cache_shape(w)
+    if dt == "f32":
+        return torch.full(shape, bits, dtype=torch.int32, device=device).view(torch.float32)
+    if dt == "f16":
+        return torch.full(shape, bits, dtype=torch.int16, device=device).view(torch.float16)
+    if dt == "bf16":
+        return torch.full(shape, bits, dtype=torch.int16, device=device).view(torch.bfloat16)
+    return torch.full(shape, bits, dtype=torch.uint8, device=device)
+
+
+def cache_bytes(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+def out_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.to(torch.float64).cpu().numpy()
+
+
+def torch_dtype(name: str):
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+class GpuStep:
+    """Uploads a workload and runs slot mapping, the cache write and decode."""
+
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        c = w.cfg
+        self.device = device
+        self.k_cache = poisoned_device_cache(w, device)
+        self.v_cache = poisoned_device_cache(w, device)
+        self.block_tables = torch.from_numpy(w.block_tables).to(device)
+        self.context_lens = torch.from_numpy(w.context_lens).to(device)
+        self.q = to_device(w.q, c.q_dtype, device)
+        self.new_k = to_device(w.new_k, c.src_dtype, device)
+        self.new_v = to_device(w.new_v, c.src_dtype, device)
+        self.new_seq = torch.from_numpy(w.new_seq).to(device)
+        self.new_pos = torch.from_numpy(w.new_pos).to(device)
+        self.out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim),
+                               dtype=torch_dtype(c.out_dtype), device=device)
+        self.kv_dtype = "fp8" if c.kv_dtype == "fp8" else None
+
+    def fill_history(self):
+        w, c = self.w, self.w.cfg
+        if w.hist_seq.size == 0:
+            self.hist_slots = torch.empty(0, dtype=torch.int64, device=self.device)
+            return
+        hs = torch.from_numpy(w.hist_seq).to(self.device)
+        hp = torch.from_numpy(w.hist_pos).to(self.device)
+        self.hist_slots = pkv.paged_kv_slot_mapping(hs, hp, self.block_tables, c.block_size)
+        hk = to_device(w.hist_k, c.src_dtype, self.device)
+        hv = to_device(w.hist_v, c.src_dtype, self.device)
+        pkv.paged_kv_write(self.hist_slots, hk, hv, self.k_cache, self.v_cache, self.kv_dtype,
+                           w.k_scale, w.v_scale)
+        del hk, hv
+
+    def write_new(self):
+        w, c = self.w, self.w.cfg
+        self.new_slots = pkv.paged_kv_slot_mapping(self.new_seq, self.new_pos, self.block_tables,
+                                                   c.block_size)
+        pkv.paged_kv_write(self.new_slots, self.new_k, self.new_v, self.k_cache, self.v_cache,
+                           self.kv_dtype, w.k_scale, w.v_scale)
+
+    def decode(self, partition_size=None, out=None, workspace=None):
+        w, c = self.w, self.w.cfg
+        part = c.partition_size if partition_size is None else partition_size
+        out = self.out if out is None else out
+        pkv.paged_attention_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
+                                   self.context_lens, w.scale, out, w.max_context_len,
+                                   partition_size=part, workspace=workspace,
+                                   kv_dtype=self.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+        return out
+
+    def run(self, partition_size=None):
+        self.fill_history()
+        self.write_new()
+        out = self.decode(partition_size)
+        torch.cuda.synchronize()
+        return out
+
+
+def assert_close_to_oracle(gpu: np.ndarray, ref: np.ndarray, kv_dtype: str, what=""):
+    """|gpu - ref| <= tol * max(1, |ref|) elementwise (tol 4e-3, fp8 KV 2e-2)."""
+    tol = TOL[kv_dtype]
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite GPU output"
+    bound = tol * np.maximum(1.0, np.abs(ref))
+    err = np.abs(gpu - ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} elements beyond tolerance; worst at {i}: "
+                             f"gpu={gpu[i]} ref={ref[i]} err={err[i]:.3e} bound={bound[i]:.3e}")
+    return float(err.max()) if err.size else 0.0

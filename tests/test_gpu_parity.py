@@ -1,0 +1,240 @@
+"""HIP path vs the oracle, through the C ABI (GPU only).
+
+Bars: slot mapping and cache writes bit-exact; decode outputs within
+4e-3 * max(1, |ref|) (2e-2 for fp8 KV) of the fp64 oracle, element by element.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_27_amd as pkv
+from gpu_helpers import (GpuStep, assert_close_to_oracle, cache_bytes, out_to_f64, to_device,
+                         torch_dtype)
+from helpers import oracle_step
+from pins import SMALL
+from workloads import CONFIGS, LLAMA8B, R70B_FP8, TINY, make_workload
+
+pytestmark = pytest.mark.gpu
+THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.load_library()
+
+
+def _oracle_all(orc, w):
+    return oracle_step(orc, w, threads=THREADS)
+
+
+# ---------------------------------------------------------------- write --------
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_slots_and_write_bit_exact(orc, name):
+    w = make_workload(SMALL[name])
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    torch.cuda.synchronize()
+    kc, vc, ns, _ = _oracle_all(orc, w)
+    if w.hist_seq.size:
+        hs = orc.slot_mapping(w.hist_seq, w.hist_pos, w.block_tables, w.cfg.block_size)
+        assert np.array_equal(g.hist_slots.cpu().numpy(), hs)
+    assert np.array_equal(g.new_slots.cpu().numpy(), ns)
+    assert np.array_equal(cache_bytes(g.k_cache).reshape(-1), kc.view(np.uint8).reshape(-1))
+    assert np.array_equal(cache_bytes(g.v_cache).reshape(-1), vc.view(np.uint8).reshape(-1))
+
+
+def test_write_fp8_every_bf16_input(orc):
+    """All 65536 bf16 bit patterns (NaN, inf, subnormals, ties) quantised by the GPU
+    write and by the oracle: identical fp8 bytes."""
+    H, D, B = 2, 128, 16
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, H, D)
+    for scale in (1.0, 0.0123, 3.5):
+        nb = 256 // B
+        kc = torch.full((nb, H, B, D), 0x7F, dtype=torch.uint8, device="cuda")
+        vc = kc.clone()
+        slots = torch.arange(256, dtype=torch.int64, device="cuda")
+        k = to_device(codes, "bf16")
+        v = to_device(codes[::-1].copy(), "bf16")
+        pkv.paged_kv_write(slots, k, v, kc, vc, "fp8", scale, scale)
+        kco = np.full((nb, H, B, D), 0x7F, np.uint8)
+        vco = kco.copy()
+        orc.kv_write(np.arange(256, dtype=np.int64), codes, codes[::-1].copy(), "bf16", kco, vco,
+                     "fp8", scale, scale)
+        assert np.array_equal(kc.cpu().numpy(), kco), scale
+        assert np.array_equal(vc.cpu().numpy(), vco), scale
+
+
+def test_write_fp8_f32_inputs(orc):
+    """fp32 sources: random values over the whole e4m3 range, exact code values,
+    midpoints (ties) and out-of-range values."""
+    H, D, B = 1, 64, 16
+    rng = np.random.default_rng(11)
+    grid = orc.fp8_to_f64(np.arange(256, dtype=np.uint8))
+    grid = np.unique(grid[np.isfinite(grid)])
+    mids = (grid[1:] + grid[:-1]) / 2
+    vals = np.concatenate([grid, mids, rng.uniform(-500, 500, 3000), rng.normal(0, 1, 3000),
+                           [np.inf, -np.inf, np.nan, 1e30, -1e-30, 0.0, -0.0]]).astype(np.float32)
+    n = (vals.size + D - 1) // D
+    vals = np.resize(vals, n * D).reshape(n, H, D)
+    nb = (n + B - 1) // B
+    kc = torch.zeros((nb, H, B, D), dtype=torch.uint8, device="cuda")
+    vc = kc.clone()
+    slots = torch.arange(n, dtype=torch.int64, device="cuda")
+    pkv.paged_kv_write(slots, to_device(vals, "f32"), to_device(vals, "f32"), kc, vc, "fp8", 1.0, 0.5)
+    kco = np.zeros((nb, H, B, D), np.uint8)
+    vco = kco.copy()
+    orc.kv_write(np.arange(n, dtype=np.int64), vals, vals, "f32", kco, vco, "fp8", 1.0, 0.5)
+    assert np.array_equal(kc.cpu().numpy(), kco)
+    assert np.array_equal(vc.cpu().numpy(), vco)
+
+
+def test_negative_slots_skip(orc):
+    w = make_workload(SMALL["llama8b"])
+    g = GpuStep(w)
+    c = w.cfg
+    before = cache_bytes(g.k_cache).copy()
+    slots = torch.full((c.num_seqs,), -1, dtype=torch.int64, device="cuda")
+    pkv.paged_kv_write(slots, g.new_k, g.new_v, g.k_cache, g.v_cache)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache_bytes(g.k_cache), before)
+
+
+# --------------------------------------------------------------- decode --------
+@pytest.mark.parametrize("mode", [None, -1, "two-blocks"], ids=["default", "single", "split"])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_decode_small(orc, name, mode):
+    w = make_workload(SMALL[name])
+    part = 2 * w.cfg.block_size if mode == "two-blocks" else mode
+    g = GpuStep(w)
+    out = out_to_f64(g.run(part))
+    _, _, _, ref = _oracle_all(orc, w)
+    assert_close_to_oracle(out, ref, w.cfg.kv_dtype, f"{name}/{mode}")
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_full_size(orc, cfg):
+    """The workload at its full size, in the launch configuration the benchmark times:
+    the whole cache after the write is compared byte by byte; decode outputs of a
+    sample of sequences (shortest, longest, and random ones; every query head)."""
+    print(f"full-size case {cfg.name} seed {cfg.seed}", flush=True)
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    out = out_to_f64(g.run())
+    kc, vc, ns, _ = oracle_step(orc, w, pairs=np.zeros((0, 2), np.int32))
+    assert np.array_equal(g.new_slots.cpu().numpy(), ns)
+    assert np.array_equal(cache_bytes(g.k_cache).reshape(-1), kc.view(np.uint8).reshape(-1))
+    assert np.array_equal(cache_bytes(g.v_cache).reshape(-1), vc.view(np.uint8).reshape(-1))
+    del g
+    c = w.cfg
+    rng = np.random.default_rng(5)
+    seqs = {int(np.argmin(w.context_lens)), int(np.argmax(w.context_lens))}
+    seqs.update(rng.choice(c.num_seqs, size=min(6, c.num_seqs), replace=False).tolist())
+    seqs = sorted(seqs)
+    pairs = np.array([(s, h) for s in seqs for h in range(c.num_q_heads)], np.int32)
+    ref = orc.decode(w.q, c.q_dtype, kc, vc, c.kv_dtype, w.block_tables, w.context_lens,
+                     w.scale, w.k_scale, w.v_scale, pairs=pairs, threads=THREADS)
+    got = out[pairs[:, 0], pairs[:, 1]]
+    assert_close_to_oracle(got, ref, c.kv_dtype, cfg.name)
+
+
+# ----------------------------------------------------------- invariances --------
+@pytest.mark.parametrize("name", ["prefix", "r70b", "llama8b"])
+def test_physical_permutation_bit_identical(name):
+    """Moving every block to another physical ID (tables rewritten) gives bit-identical output."""
+    w = make_workload(SMALL[name])
+    g = GpuStep(w)
+    out1 = g.run().clone()
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(w.num_blocks)).cuda()
+    inv = torch.argsort(perm)
+    g.k_cache = g.k_cache[inv].contiguous()  # new block perm[b] holds old block b
+    g.v_cache = g.v_cache[inv].contiguous()
+    g.block_tables = perm[g.block_tables.long()].to(torch.int32).contiguous()
+    out2 = g.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+
+
+def test_split_matches_single():
+    cfg = LLAMA8B.replace(num_seqs=6, ctx_params=(300, 1700), out_dtype="f32")
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    single = g.decode(-1).clone()
+    for part in (16, 64, 512):
+        split = g.decode(part).clone()
+        torch.cuda.synchronize()
+        assert (split - single).abs().max().item() <= 1e-5, part
+
+
+# ------------------------------------------------------------- edge cases --------
+EDGE = {
+    "ctx-edges-b16": LLAMA8B.replace(num_seqs=9, ctx_kind="fixed",
+                                     ctx_params=(1, 15, 16, 17, 31, 32, 33, 512, 513)),
+    "ctx-edges-b32": LLAMA8B.replace(num_seqs=8, block_size=32, ctx_kind="fixed",
+                                     ctx_params=(1, 16, 31, 32, 33, 64, 65, 1025)),
+    "ctx-zero": LLAMA8B.replace(num_seqs=3, ctx_kind="fixed", ctx_params=(0, 5, 0)),
+    "mha": LLAMA8B.replace(num_seqs=3, num_q_heads=4, num_kv_heads=4, ctx_params=(20, 300)),
+    "g3": LLAMA8B.replace(num_seqs=3, num_q_heads=6, num_kv_heads=2, ctx_params=(20, 300)),
+    "g16": LLAMA8B.replace(num_seqs=3, num_q_heads=32, num_kv_heads=2, ctx_params=(20, 300)),
+    "mqa-g8": LLAMA8B.replace(num_seqs=3, num_q_heads=8, num_kv_heads=1, ctx_params=(20, 300)),
+    "d64-bf16": LLAMA8B.replace(num_seqs=3, head_dim=64, ctx_params=(20, 300)),
+    "f16": LLAMA8B.replace(num_seqs=3, q_dtype="f16", kv_dtype="f16", src_dtype="f16",
+                           out_dtype="f16", ctx_params=(20, 300)),
+    "fp8-f16q": R70B_FP8.replace(num_seqs=3, q_dtype="f16", src_dtype="f16", out_dtype="f16",
+                                 ctx_params=(100, 0.8, 16, 600)),
+    "fp8-d64-b32": R70B_FP8.replace(num_seqs=3, head_dim=64, block_size=32, num_q_heads=16,
+                                    ctx_params=(100, 0.8, 16, 600)),
+    "fp32-d128": TINY.replace(head_dim=128, pool_blocks=0),
+    "fp8-out-f32": R70B_FP8.replace(num_seqs=3, out_dtype="f32", ctx_params=(100, 0.8, 16, 600)),
+}
+
+
+@pytest.mark.parametrize("mode", [None, "two-blocks"], ids=["default", "split"])
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_cases(orc, name, mode):
+    w = make_workload(EDGE[name])
+    part = 2 * w.cfg.block_size if mode else None
+    out = out_to_f64(GpuStep(w).run(part))
+    _, _, _, ref = _oracle_all(orc, w)
+    assert_close_to_oracle(out, ref, w.cfg.kv_dtype, name)
+    if name == "ctx-zero":
+        assert (out[0] == 0).all() and (out[2] == 0).all()
+
+
+def test_empty_batch():
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    cl = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    pkv.paged_attention_decode(q, kc, kc, bt, cl, 0.1, out, 0)
+
+
+def test_fp8_value_codes_exact(orc):
+    """One cached token whose V holds every e4m3fn code: with one token the weight is
+    exactly 1, so out (fp32) = code * v_scale, NaN codes giving NaN."""
+    H, D, B = 2, 128, 16
+    vcodes = np.arange(256, dtype=np.uint8).reshape(H, D)
+    kc = np.full((2, H, B, D), 0x7F, np.uint8)
+    vc = kc.copy()
+    kc[1, :, 0, :] = 0x38  # K = 1.0
+    vc[1, :, 0, :] = vcodes
+    bt = np.array([[1]], np.int32)
+    cl = np.array([1], np.int32)
+    q = np.random.default_rng(1).standard_normal((1, 4, D)).astype(np.float32)
+    qb = torch.from_numpy(q).to(torch.bfloat16)
+    out = torch.empty((1, 4, D), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_decode(qb.cuda(), torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(),
+                               torch.from_numpy(bt).cuda(), torch.from_numpy(cl).cuda(), 0.1, out,
+                               1, kv_dtype="fp8", k_scale=0.5, v_scale=0.25)
+    got = out.cpu().numpy().astype(np.float64)
+    qbits = qb.view(torch.int16).numpy().view(np.uint16)
+    ref = orc.decode(qbits, "bf16", kc, vc, "fp8", bt, cl, 0.1, 0.5, 0.25)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])  # one fp32 rounding of an exact product
