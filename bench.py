@@ -44,12 +44,14 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama3-8b-shaped-bf16-64seq",
                     help="workload name or 1-based index (default: the 8B-shaped layer)")
-    ap.add_argument("--reps", type=int, default=30, help="cold-cache reps of the roofline leg")
+    ap.add_argument("--reps", type=int, default=30, help="cold-cache reps of the roofline leg (>= 1)")
     ap.add_argument("--all", action="store_true", help="also measure every other workload (stderr + --json-out)")
     ap.add_argument("--json-out", default=None, help="write per-workload results here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the oracle leg")
     ap.add_argument("--partition", type=int, default=None, help="override the partition size")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy --steps times (counter calibration)")
     return ap.parse_args()
 
 
@@ -117,8 +119,12 @@ class Step:
         self.slots = torch.empty(c.num_seqs, dtype=torch.int64, device=dev)
         self.out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=tdt[c.out_dtype], device=dev)
         self.partition = c.partition_size if partition is None else partition
-        need = pkv.paged_attention_workspace_size(c.num_seqs, c.num_q_heads, c.head_dim,
-                                                  w.max_context_len, c.block_size, self.partition)
+        self.desc = pkv.cache_desc(self.k_cache, self.kv_dtype, w.k_scale, w.v_scale)
+        need = pkv.paged_attention_workspace_size(self.desc, c.q_dtype, c.num_seqs, c.num_q_heads,
+                                                  w.max_context_len, self.partition)
+        self.schedule = pkv.paged_attention_schedule(self.desc, c.q_dtype, c.num_seqs,
+                                                     c.num_q_heads, w.max_context_len,
+                                                     self.partition)
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         # history: every cached token written once through the same write kernel
         if w.hist_seq.size:
@@ -190,12 +196,14 @@ def measure(cfg, args, partition=None):
     t2 = time.perf_counter()
     ms_step = (t2 - t1) * 1e3 / args.steps
 
-    # Cold-cache leg: L2 and MALL flushed before each rep; HIP events on the stream the
+    # Cold-cache leg: L2 and MALL flushed before each rep by reading 1 GiB (a read leaves
+    # no dirty lines to write back during the timed call); HIP events on the stream the
     # library launches on (torch's current stream, which the binding passes down).
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.reps)]
     for r in range(args.reps):
-        flush.random_(0, 255) if r == 0 else flush.add_(1)
+        sink.copy_(flush.sum())
         e = ev[r]
         e[0].record()
         st.slot_map()
@@ -211,10 +219,6 @@ def measure(cfg, args, partition=None):
     del flush
     dec_ms = float(np.mean(t_dec))
     achieved = nbytes["decode"] / (dec_ms * 1e-3) / 1e9
-    part = st.partition
-    if part == 0:
-        part = st.pkv.paged_attention_auto_partition(cfg.num_seqs, cfg.num_kv_heads,
-                                                     w.max_context_len, cfg.block_size)
     res = {
         "workload": cfg.name, "ms_per_step": ms_step,
         "step_GBps": nbytes["step"] / (ms_step * 1e-3) / 1e9,
@@ -225,12 +229,12 @@ def measure(cfg, args, partition=None):
         "write_ms_cold_mean": float(np.mean(t_write)), "slotmap_ms_cold_mean": float(np.mean(t_slot)),
         "decode_GBps_cold": achieved, "decode_frac_hbm_peak": achieved / HBM_PEAK_GBS,
         "decode_unique_GBps_cold": (nbytes["decode"] - nbytes["kv"] + nbytes["kv_unique"]) / (dec_ms * 1e-3) / 1e9,
-        "bytes": nbytes, "partition": int(part) if part and part > 0 else "single-pass",
+        "bytes": nbytes, "schedule": st.schedule,
         "max_context_len": w.max_context_len, "sum_context": int(w.context_lens.sum()),
     }
     log(f"[{cfg.name}] step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s), decode cold "
         f"{dec_ms * 1e3:.1f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak), "
-        f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, partition {res['partition']}")
+        f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, schedule {res['schedule']}")
     return w, st, res
 
 
@@ -269,6 +273,7 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse_args()
+    args.reps = max(1, args.reps)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this path has "
@@ -280,6 +285,14 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     pkv.load_library()  # raises if the HIP library is missing: there is no fallback
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.steps} x {src.numel() * 4} bytes")
+        return
     cfg = pick_config(args.config)
     w, st, res = measure(cfg, args)
     del st
@@ -308,7 +321,7 @@ def main():
                    "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
                    "block_size": c.block_size, "q_dtype": c.q_dtype, "kv_dtype": c.kv_dtype,
                    "context_lens": f"{c.ctx_kind}{tuple(c.ctx_params)}",
-                   "sum_context": res["sum_context"], "partition": res["partition"],
+                   "sum_context": res["sum_context"], "schedule": res["schedule"],
                    "seed": c.seed},
         "pct_hbm_peak": round(100 * res["step_GBps"] / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(res["seq_heads_per_s"], 1),

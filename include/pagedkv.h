@@ -100,11 +100,27 @@ int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* 
                    const void* v, pkv_dtype src_dtype, void* k_cache, void* v_cache,
                    const pkv_cache_desc* cache, hipStream_t stream);
 
-/* Bytes of workspace paged_attention_decode needs for this shape (0 if the call
- * runs in a single pass).  partition_size as for paged_attention_decode. */
-size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                      int32_t max_context_len, int32_t block_size,
-                                      int32_t partition_size);
+/*
+ * How paged_attention_decode schedules a call with these arguments.  Returns the
+ * schedule (0 = one pass per (sequence, KV head), 1 = fixed partitions merged by a
+ * log-sum-exp pass, 2 = balanced: equal shares of 16-token chunks per resident
+ * wave, partials merged by a log-sum-exp pass) or a negative pkv_status.
+ * *partition_out gets the tokens per partition (0 for the balanced schedule),
+ * *workers_out the waves of a balanced launch (0 otherwise); either may be NULL.
+ * The balanced schedule sizes itself for the current device (a full MI355X when
+ * no device is visible).
+ */
+int32_t paged_attention_schedule(const pkv_cache_desc* cache, pkv_dtype q_dtype,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_size, int32_t* partition_out,
+                                 int32_t* workers_out);
+
+/* Bytes of device workspace paged_attention_decode needs for these arguments (0 for
+ * one pass, or when the arguments are invalid).  Arguments as for
+ * paged_attention_decode. */
+size_t paged_attention_workspace_size(const pkv_cache_desc* cache, pkv_dtype q_dtype,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_context_len, int32_t partition_size);
 
 /*
  * out[s][h][:] = softmax_t(scale * q[s][h] . K_t) V_t over t = 0 .. context_lens[s]-1,
@@ -120,11 +136,13 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
  *   context_lens : int32 [num_seqs], counting the new token (already written)
  *   max_context_len : host-side upper bound of context_lens (sizes the grid)
  *   out          : [num_seqs][num_q_heads][head_dim] of out_dtype (f32/f16/bf16)
- *   partition_size : 0 = library's choice; -1 = one pass per (sequence, KV head);
+ *   partition_size : 0 = balanced schedule (up to 8191 sequences; fixed 512-token
+ *                    partitions beyond); -1 = one pass per (sequence, KV head);
  *                    else tokens per partition, a positive multiple of block_size;
  *                    partial results are merged by a log-sum-exp pass
- *   workspace    : device scratch of >= paged_attention_workspace_size() bytes
- *                  (may be NULL when that size is 0)
+ *   workspace    : device scratch of >= paged_attention_workspace_size() bytes,
+ *                  256-byte aligned (may be NULL when that size is 0); its contents
+ *                  on entry do not matter; calls sharing one workspace must not overlap
  * Supported: head_dim 64 or 128; block_size 16 or 32; group size
  * num_q_heads / num_kv_heads in 1..16; (q, cache) dtypes (f32, f32), (f16, f16),
  * (bf16, bf16), (bf16 or f16, fp8).  Accumulation is fp32; the output is rounded
@@ -139,11 +157,6 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
                            int32_t max_context_len, float scale, void* out,
                            pkv_dtype out_dtype, int32_t partition_size, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
-
-/* Partition size (tokens) paged_attention_decode uses for partition_size == 0,
- * or 0 if it runs a single pass. */
-int32_t paged_attention_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
-                                       int32_t max_context_len, int32_t block_size);
 
 /* Static description of a status code. */
 const char* pkv_status_string(int status);

@@ -4,11 +4,11 @@ The compute runs in libpagedkv.so (hand-written HIP kernels behind the C ABI
 declared in include/pagedkv.h); this package only marshals torch tensors to it.
 """
 from ._binding import (BF16, F16, F32, FP8_E4M3, CacheDesc, PagedKVError, cache_desc,
-                       load_library, paged_attention_auto_partition, paged_attention_decode,
+                       load_library, paged_attention_schedule, paged_attention_decode,
                        paged_attention_workspace_size, paged_kv_slot_mapping, paged_kv_write,
                        pkv_abi_version, pkv_status_string)
 
 __all__ = ["BF16", "F16", "F32", "FP8_E4M3", "CacheDesc", "PagedKVError", "cache_desc",
-           "load_library", "paged_attention_auto_partition", "paged_attention_decode",
+           "load_library", "paged_attention_schedule", "paged_attention_decode",
            "paged_attention_workspace_size", "paged_kv_slot_mapping", "paged_kv_write",
            "pkv_abi_version", "pkv_status_string"]

@@ -22,9 +22,10 @@ _NAME_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8_E4M3}
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHAPE",
           -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH"}
 
-EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_workspace_size",
-            "paged_attention_decode", "paged_attention_auto_partition", "pkv_status_string",
+EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_schedule",
+            "paged_attention_workspace_size", "paged_attention_decode", "pkv_status_string",
             "pkv_abi_version"]
+SCHEDULES = {0: "single-pass", 1: "fixed-partitions", 2: "balanced"}
 
 
 class CacheDesc(ctypes.Structure):
@@ -59,14 +60,16 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_kv_write.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp,
                                    ctypes.POINTER(CacheDesc), vp]
     lib.paged_kv_write.restype = ctypes.c_int
-    lib.paged_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_workspace_size.argtypes = [ctypes.POINTER(CacheDesc), ctypes.c_int, i32,
+                                                   i32, i32, i32]
     lib.paged_attention_workspace_size.restype = ctypes.c_size_t
+    lib.paged_attention_schedule.argtypes = [ctypes.POINTER(CacheDesc), ctypes.c_int, i32, i32,
+                                             i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.paged_attention_schedule.restype = i32
     lib.paged_attention_decode.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp,
                                            ctypes.POINTER(CacheDesc), vp, i32, vp, i32, f32, vp,
                                            ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
     lib.paged_attention_decode.restype = ctypes.c_int
-    lib.paged_attention_auto_partition.argtypes = [i32, i32, i32, i32]
-    lib.paged_attention_auto_partition.restype = i32
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -151,18 +154,23 @@ def paged_kv_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
 
 
-def paged_attention_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
-                                   max_context_len: int, block_size: int,
-                                   partition_size: int = 0) -> int:
-    return int(load_library().paged_attention_workspace_size(num_seqs, num_q_heads, head_dim,
-                                                             max_context_len, block_size,
-                                                             partition_size))
+def paged_attention_workspace_size(desc: CacheDesc, q_dtype, num_seqs: int, num_q_heads: int,
+                                   max_context_len: int, partition_size: int = 0) -> int:
+    return int(load_library().paged_attention_workspace_size(
+        ctypes.byref(desc), dtype_code(q_dtype), num_seqs, num_q_heads, max_context_len,
+        partition_size))
 
 
-def paged_attention_auto_partition(num_seqs: int, num_kv_heads: int, max_context_len: int,
-                                   block_size: int) -> int:
-    return int(load_library().paged_attention_auto_partition(num_seqs, num_kv_heads,
-                                                             max_context_len, block_size))
+def paged_attention_schedule(desc: CacheDesc, q_dtype, num_seqs: int, num_q_heads: int,
+                             max_context_len: int, partition_size: int = 0) -> dict:
+    """The schedule a decode call with these arguments uses."""
+    part, workers = ctypes.c_int32(0), ctypes.c_int32(0)
+    mode = load_library().paged_attention_schedule(ctypes.byref(desc), dtype_code(q_dtype),
+                                                   num_seqs, num_q_heads, max_context_len,
+                                                   partition_size, ctypes.byref(part),
+                                                   ctypes.byref(workers))
+    _check("paged_attention_schedule", min(mode, 0))
+    return {"schedule": SCHEDULES[mode], "partition": part.value, "workers": workers.value}
 
 
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -176,14 +184,14 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     lib = load_library()
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
     n, hq, d = q.shape
-    need = paged_attention_workspace_size(n, hq, d, max_context_len, desc.block_size,
-                                          partition_size)
+    qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
+    need = paged_attention_workspace_size(desc, qd, n, hq, max_context_len, partition_size)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     _check("paged_attention_decode",
            lib.paged_attention_decode(
-               _ptr(q), dtype_code(q_dtype if q_dtype is not None else q.dtype), n, hq,
+               _ptr(q), qd, n, hq,
                _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
                block_tables.shape[1], _ptr(context_lens), int(max_context_len), float(scale),
                _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),

@@ -1,4 +1,4 @@
-// C ABI layer: host-side argument checks, partition choice, workspace carving and
+// C ABI layer: host-side argument checks, schedule choice, workspace carving and
 // dispatch to the gfx950 kernels.  Declarations and contracts: include/pagedkv.h.
 #include "pagedkv.h"
 
@@ -22,41 +22,76 @@ int check_cache(const pkv_cache_desc* c) {
   return PKV_OK;
 }
 
-// Tokens per partition for partition_size == 0.  Each (sequence, KV head) with a
-// context longer than 512 tokens is cut into 512-token partitions: enough
-// workgroups to fill 256 compute units even for a handful of sequences, and a
-// partial-result overhead (G * (d_h + 2) floats per partition) under 1% of the
-// K/V bytes a partition reads.
-int32_t auto_partition(int32_t max_context_len, int32_t block_size) {
-  const int32_t p = 512;
-  if (max_context_len <= p) return 0;
-  return (p / block_size) * block_size;
+int check_decode_shape(const pkv_cache_desc* cache, int q_dtype, int out_dtype, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t max_context_len) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (!known_dtype(q_dtype) || !known_dtype(out_dtype)) return PKV_ERR_DTYPE;
+  if (q_dtype == PKV_FP8_E4M3 || out_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (cache->dtype == PKV_FP8_E4M3) {
+    if (q_dtype != PKV_BF16 && q_dtype != PKV_F16) return PKV_ERR_DTYPE;
+  } else if (cache->dtype != q_dtype) {
+    return PKV_ERR_DTYPE;
+  }
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
+  if (num_seqs > 65535 || cache->num_kv_heads > 65535) return PKV_ERR_SHAPE;
+  if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_HEADS;
+  const int32_t G = num_q_heads / cache->num_kv_heads;
+  if (G < 1 || G > 16) return PKV_ERR_SHAPE;
+  return PKV_OK;
 }
 
+// How a decode call is scheduled.
+enum Mode { kSingle = 0, kFixed = 1, kBalanced = 2 };
+
 struct Plan {
-  int32_t partition;
-  int32_t parts;
+  Mode mode;
+  int32_t partition;  // tokens per partition (fixed / single)
+  int32_t parts;      // partitions in the grid (fixed / single)
+  int32_t workers;    // waves in the launch (balanced)
+  size_t ws_bytes;
 };
 
-int plan_partitions(int32_t requested, int32_t max_context_len, int32_t block_size, Plan* out) {
+// partition_size == 0 picks the balanced schedule (up to kStreamKMaxSeqs sequences;
+// beyond that, fixed 512-token partitions); -1 one pass per (sequence, KV head);
+// > 0 fixed partitions of that many tokens (a multiple of the block size).
+int plan_decode(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                int32_t max_context_len, int32_t requested, Plan* out) {
+  const int32_t bs = c->block_size;
+  const int32_t G = num_q_heads / c->num_kv_heads;
+  if (requested == 0 && num_seqs <= pkv::kStreamKMaxSeqs) {
+    const int w = pkv::streamk_workers(c->dtype, q_dtype, c->head_dim, G, num_seqs);
+    if (w <= 0) return PKV_ERR_DTYPE;
+    out->mode = kBalanced;
+    out->partition = 0;
+    out->parts = 0;
+    out->workers = w;
+    out->ws_bytes = pkv::streamk_ws_bytes(num_seqs, G, c->head_dim, w);
+    return PKV_OK;
+  }
   int32_t p;
   if (requested == -1) {
     p = 0;
   } else if (requested == 0) {
-    p = auto_partition(max_context_len, block_size);
+    p = (512 / bs) * bs;
   } else {
-    if (requested < 0 || requested % block_size != 0) return PKV_ERR_WORKSPACE;
+    if (requested < 0 || requested % bs != 0) return PKV_ERR_WORKSPACE;
     p = requested;
   }
+  out->workers = 0;
   if (p == 0 || max_context_len <= p) {
-    // single pass: one partition spanning the longest context
-    int32_t span = max_context_len > 0 ? max_context_len : block_size;
-    span = (span + block_size - 1) / block_size * block_size;
+    // one pass: a single partition spanning the longest context
+    int32_t span = max_context_len > 0 ? max_context_len : bs;
+    span = (span + bs - 1) / bs * bs;
+    out->mode = kSingle;
     out->partition = span;
     out->parts = 1;
+    out->ws_bytes = 0;
   } else {
+    out->mode = kFixed;
     out->partition = p;
     out->parts = (max_context_len + p - 1) / p;
+    out->ws_bytes = pkv::ws_total_bytes(num_seqs, num_q_heads, c->head_dim, out->parts);
   }
   return PKV_OK;
 }
@@ -65,7 +100,7 @@ int plan_partitions(int32_t requested, int32_t max_context_len, int32_t block_si
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 1; }
+int32_t pkv_abi_version(void) { return 2; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -121,22 +156,29 @@ int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* 
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
-int32_t paged_attention_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
-                                       int32_t max_context_len, int32_t block_size) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  if (block_size <= 0) return 0;
-  return auto_partition(max_context_len, block_size);
+int32_t paged_attention_schedule(const pkv_cache_desc* cache, pkv_dtype q_dtype,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_size, int32_t* partition_out,
+                                 int32_t* workers_out) {
+  int st = check_decode_shape(cache, q_dtype, q_dtype, num_seqs, num_q_heads, max_context_len);
+  if (st) return st;
+  Plan plan;
+  st = plan_decode(cache, q_dtype, num_seqs, num_q_heads, max_context_len, partition_size, &plan);
+  if (st) return st;
+  if (partition_out) *partition_out = plan.partition;
+  if (workers_out) *workers_out = plan.workers;
+  return plan.mode;
 }
 
-size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                      int32_t max_context_len, int32_t block_size,
-                                      int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || block_size <= 0) return 0;
+size_t paged_attention_workspace_size(const pkv_cache_desc* cache, pkv_dtype q_dtype,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_context_len, int32_t partition_size) {
+  if (check_decode_shape(cache, q_dtype, q_dtype, num_seqs, num_q_heads, max_context_len)) return 0;
+  if (num_seqs == 0) return 0;
   Plan plan;
-  if (plan_partitions(partition_size, max_context_len, block_size, &plan)) return 0;
-  if (plan.parts <= 1) return 0;
-  return pkv::ws_total_bytes(num_seqs, num_q_heads, head_dim, plan.parts);
+  if (plan_decode(cache, q_dtype, num_seqs, num_q_heads, max_context_len, partition_size, &plan))
+    return 0;
+  return plan.ws_bytes;
 }
 
 int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
@@ -146,29 +188,21 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
                            int32_t max_context_len, float scale, void* out,
                            pkv_dtype out_dtype, int32_t partition_size, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-  int st = check_cache(cache);
+  int st = check_decode_shape(cache, q_dtype, out_dtype, num_seqs, num_q_heads, max_context_len);
   if (st) return st;
-  if (!known_dtype(q_dtype) || !known_dtype(out_dtype)) return PKV_ERR_DTYPE;
-  if (q_dtype == PKV_FP8_E4M3 || out_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (cache->dtype == PKV_FP8_E4M3) {
-    if (q_dtype != PKV_BF16 && q_dtype != PKV_F16) return PKV_ERR_DTYPE;
-  } else if (cache->dtype != q_dtype) {
-    return PKV_ERR_DTYPE;
-  }
-  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_blocks_per_seq <= 0)
-    return PKV_ERR_SHAPE;
-  if (num_seqs > 65535 || cache->num_kv_heads > 65535) return PKV_ERR_SHAPE;
-  if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_HEADS;
-  const int32_t G = num_q_heads / cache->num_kv_heads;
-  if (G < 1 || G > 16) return PKV_ERR_SHAPE;
+  if (max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
 
   Plan plan;
-  st = plan_partitions(partition_size, max_context_len, cache->block_size, &plan);
+  st = plan_decode(cache, q_dtype, num_seqs, num_q_heads, max_context_len, partition_size, &plan);
   if (st) return st;
+  if (plan.ws_bytes) {
+    if (!workspace) return PKV_ERR_NULL;
+    if (workspace_bytes < plan.ws_bytes || ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
+  }
 
   pkv::DecodeArgs a;
   a.q = q;
@@ -193,16 +227,20 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
   a.partition = plan.partition;
   a.num_partitions = plan.parts;
   a.ws_m = a.ws_l = a.ws_acc = nullptr;
-  if (plan.parts > 1) {
-    const size_t need = pkv::ws_total_bytes(num_seqs, num_q_heads, cache->head_dim, plan.parts);
-    if (!workspace) return PKV_ERR_NULL;
-    if (workspace_bytes < need || ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
+  a.sk_workers = plan.workers;
+  a.sk_cum = nullptr;
+  a.sk_part = nullptr;
+  if (plan.mode == kFixed) {
     const size_t ml = pkv::ws_ml_bytes(num_seqs, num_q_heads, plan.parts);
     a.ws_m = (float*)workspace;
     a.ws_l = (float*)((char*)workspace + ml);
     a.ws_acc = (float*)((char*)workspace + 2 * ml);
+  } else if (plan.mode == kBalanced) {
+    a.sk_cum = (int32_t*)workspace;
+    a.sk_part = (float*)((char*)workspace + pkv::align256((size_t)(num_seqs + 1) * sizeof(int)));
   }
-  hipError_t e = pkv::launch_decode(a, stream);
+  hipError_t e = plan.mode == kBalanced ? pkv::launch_decode_streamk(a, stream)
+                                        : pkv::launch_decode(a, stream);
   if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }

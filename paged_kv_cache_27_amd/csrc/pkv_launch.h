@@ -40,14 +40,27 @@ struct DecodeArgs {
   float* ws_m;             // [N][H_q][P] running max (log2 domain), split mode only
   float* ws_l;             // [N][H_q][P] softmax denominators
   float* ws_acc;           // [N][H_q][P][D] unnormalised outputs
+  // balanced schedule
+  int32_t sk_workers;      // waves in the launch
+  int32_t* sk_cum;         // [N + 1] chunk prefix, written by the decode kernel
+  float* sk_part;          // [2 * workers][2 * GP + GP * D] partials
 };
 
 hipError_t launch_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t n,
                                const int32_t* block_tables, int32_t max_blocks,
                                int32_t block_size, int64_t* slots, hipStream_t stream);
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
-// Returns hipErrorInvalidValue for an unsupported combination (checked earlier by the ABI).
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Return hipErrorInvalidValue for an unsupported combination (checked earlier by the ABI).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);          // fixed partitions
+hipError_t launch_decode_streamk(const DecodeArgs& a, hipStream_t stream);  // balanced
+
+// Balanced schedule: resident waves of the chosen kernel on the current device (a
+// full MI355X if no device is visible), 0 for an unsupported combination; and the
+// workspace it needs.  The sequence count is capped by the LDS prefix array.
+constexpr int kStreamKMaxSeqs = 8191;
+int pad_group(int G);
+int streamk_workers(int cache_dtype, int q_dtype, int head_dim, int group, int num_seqs);
+size_t streamk_ws_bytes(int num_seqs, int group, int head_dim, int workers);
 
 // Workspace layout for split mode, each array 256-byte aligned.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

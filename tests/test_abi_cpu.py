@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pkv.pkv_abi_version() == 1
+    assert pkv.pkv_abi_version() == 2
 
 
 def test_status_strings():
@@ -64,20 +64,30 @@ def test_decode_argument_errors():
     assert _decode(lib, _desc(), maxb=2, maxctx=40) == -3  # table too short for max_context_len
     assert _decode(lib, _desc(), maxb=40, maxctx=600, part=24) == -5  # not a multiple of B
     assert _decode(lib, _desc(), maxb=40, maxctx=600, part=32) == -1  # split needs a workspace
-    need = pkv.paged_attention_workspace_size(2, 4, 128, 600, 16, 32)
+    need = pkv.paged_attention_workspace_size(_desc(), pkv.BF16, 2, 4, 600, 32)
     assert need > 0
     assert _decode(lib, _desc(), maxb=40, maxctx=600, part=32, ws=FAKE, wsb=need - 1) == -5
     assert _decode(lib, _desc(), n=0) == 0  # empty batch: nothing to do
 
 
-def test_workspace_sizes():
-    assert pkv.paged_attention_workspace_size(8, 32, 128, 512, 16, 0) == 0  # fits one pass
-    assert pkv.paged_attention_workspace_size(8, 32, 128, 32768, 16, -1) == 0
-    ws = pkv.paged_attention_workspace_size(8, 32, 128, 32768, 16, 512)
+def test_workspace_sizes_and_schedules():
+    d = _desc(num_kv_heads=8)
+    assert pkv.paged_attention_workspace_size(d, pkv.BF16, 8, 32, 32768, -1) == 0  # one pass
+    assert pkv.paged_attention_workspace_size(d, pkv.BF16, 8, 32, 512, 512) == 0  # fits one partition
+    ws = pkv.paged_attention_workspace_size(d, pkv.BF16, 8, 32, 32768, 512)
     # m and l ([N][H_q][P] fp32 each) plus acc ([N][H_q][P][d_h] fp32)
     assert ws >= 8 * 32 * 64 * (128 + 2) * 4
-    assert pkv.paged_attention_auto_partition(64, 8, 4096, 16) == 512
-    assert pkv.paged_attention_auto_partition(64, 8, 300, 16) == 0
+    sch = pkv.paged_attention_schedule(d, pkv.BF16, 8, 32, 32768, 512)
+    assert sch == {"schedule": "fixed-partitions", "partition": 512, "workers": 0}
+    sch = pkv.paged_attention_schedule(d, pkv.BF16, 64, 32, 4096, 0)
+    assert sch["schedule"] == "balanced" and sch["workers"] > 0 and sch["workers"] % 4 == 0
+    # balanced: chunk prefix (N+1 ints) and two partials per wave (m, l, acc for 4 heads)
+    ws = pkv.paged_attention_workspace_size(d, pkv.BF16, 64, 32, 4096, 0)
+    assert ws >= 2 * sch["workers"] * (2 * 4 + 4 * 128) * 4
+    assert pkv.paged_attention_schedule(d, pkv.BF16, 8, 32, 300, -1)["schedule"] == "single-pass"
+    assert pkv.paged_attention_schedule(d, pkv.BF16, 9000, 32, 3000, 0)["schedule"] == "fixed-partitions"
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_schedule(d, pkv.F16, 8, 32, 300, 0)  # q dtype != cache dtype
 
 
 def test_write_argument_errors():
