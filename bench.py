@@ -30,7 +30,9 @@ if str(ROOT) not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective KV GB/s (% of HBM peak) and seq-heads/s per decode layer"
 DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
-KERNEL_SOURCES = ["paged_kv_cache_27_amd/csrc/decode.hip", "paged_kv_cache_27_amd/csrc/pkv_device.h"]
+KERNEL_SOURCES = ["paged_kv_cache_27_amd/csrc/decode.hip", "paged_kv_cache_27_amd/csrc/decode_sk.hip",
+                  "paged_kv_cache_27_amd/csrc/decode_common.h", "paged_kv_cache_27_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_27_amd/csrc/pkv_launch.h", "paged_kv_cache_27_amd/csrc/api.cpp"]
 
 
 def log(*a):
@@ -159,6 +161,13 @@ class Step:
         self.decode()
 
 
+KERNEL_LABEL = {
+    "balanced": "paged_attention_decode call (decode_sk_kernel + merge_sk_kernel)",
+    "fixed-partitions": "paged_attention_decode call (decode_kernel + merge_kernel)",
+    "single-pass": "paged_attention_decode call (decode_kernel)",
+}
+
+
 def traffic_for(cfg_name):
     """HBM bytes per decode call from the committed rocprofv3 counter summary, if it was
     taken on the current kernel sources; else None."""
@@ -253,22 +262,29 @@ def cpu_baseline(w, budget_s):
     ns = orc.slot_mapping(w.new_seq, w.new_pos, w.block_tables, c.block_size)
     orc.kv_write(ns, w.new_k, w.new_v, c.src_dtype, kc, vc, c.kv_dtype, w.k_scale, w.v_scale)
     threads = min(16, len(os.sched_getaffinity(0)))
-    done_seqs, elapsed, tokens = 0, 0.0, 0
+    # Whole passes over the workload (all sequences, all query heads) until the budget is
+    # spent; the last pass may stop early at a sequence boundary.
+    passes, elapsed, tokens, seq_heads = 0, 0.0, 0, 0
     per = max(1, threads // 2)
-    while done_seqs < c.num_seqs and elapsed < budget_s:
-        seqs = range(done_seqs, min(c.num_seqs, done_seqs + per))
-        pairs = np.array([(s, h) for s in seqs for h in range(c.num_q_heads)], np.int32)
-        t0 = time.perf_counter()
-        orc.decode(w.q, c.q_dtype, kc, vc, c.kv_dtype, w.block_tables, w.context_lens, w.scale,
-                   w.k_scale, w.v_scale, pairs=pairs, threads=threads)
-        elapsed += time.perf_counter() - t0
-        tokens += int(w.context_lens[list(seqs)].sum())
-        done_seqs = seqs[-1] + 1
+    while elapsed < budget_s:
+        s0 = 0
+        while s0 < c.num_seqs and elapsed < budget_s:
+            seqs = range(s0, min(c.num_seqs, s0 + per))
+            pairs = np.array([(s, h) for s in seqs for h in range(c.num_q_heads)], np.int32)
+            t0 = time.perf_counter()
+            orc.decode(w.q, c.q_dtype, kc, vc, c.kv_dtype, w.block_tables, w.context_lens,
+                       w.scale, w.k_scale, w.v_scale, pairs=pairs, threads=threads)
+            elapsed += time.perf_counter() - t0
+            tokens += int(w.context_lens[list(seqs)].sum())
+            seq_heads += len(seqs) * c.num_q_heads
+            s0 = seqs[-1] + 1
+        passes += s0 / c.num_seqs
     kv_bytes = tokens * c.num_kv_heads * c.head_dim * 2 * DT_BYTES[c.kv_dtype]
     return {"value": kv_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seq_heads_per_s": done_seqs * c.num_q_heads / elapsed,
-            "sample": f"decode of sequences 0..{done_seqs - 1} of {c.num_seqs} (all {c.num_q_heads} "
-                      f"query heads, {tokens} context tokens), fp64, {elapsed:.1f}s wall on {threads} threads"}
+            "seq_heads_per_s": seq_heads / elapsed,
+            "sample": f"{passes:.2f} passes of the decode over all {c.num_seqs} sequences x "
+                      f"{c.num_q_heads} query heads ({tokens} context tokens in total), fp64, "
+                      f"{elapsed:.1f}s wall on {threads} threads"}
 
 
 def main():
@@ -328,7 +344,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(res["decode_GBps_cold"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["decode_frac_hbm_peak"], 4), "traffic": traffic,
-                     "kernel": "paged_attention_decode call (decode_kernel + merge_kernel)",
+                     "kernel": KERNEL_LABEL.get(res["schedule"]["schedule"], "?"),
                      "bytes_per_launch": res["bytes"]["decode"],
                      "mean_launch_ms": round(res["decode_ms_cold_mean"], 6)},
         "cpu_baseline": cpu,
