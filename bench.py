@@ -121,13 +121,15 @@ class Step:
         self.slots = torch.empty(c.num_seqs, dtype=torch.int64, device=dev)
         self.out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=tdt[c.out_dtype], device=dev)
         self.partition = c.partition_size if partition is None else partition
-        self.desc = pkv.cache_desc(self.k_cache, self.kv_dtype, w.k_scale, w.v_scale)
+        # prefix sharing maps many sequences to one physical block: say so (cache policy)
+        self.shared = bool(w.shared_blocks)
+        self.desc = pkv.cache_desc(self.k_cache, self.kv_dtype, w.k_scale, w.v_scale, self.shared)
         need = pkv.paged_attention_workspace_size(self.desc, c.q_dtype, c.num_seqs, c.num_q_heads,
                                                   w.max_context_len, self.partition)
         self.schedule = pkv.paged_attention_schedule(self.desc, c.q_dtype, c.num_seqs,
                                                      c.num_q_heads, w.max_context_len,
                                                      self.partition)
-        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
         # history: every cached token written once through the same write kernel
         if w.hist_seq.size:
             hs = torch.from_numpy(w.hist_seq).to(dev)
@@ -153,7 +155,8 @@ class Step:
         self.pkv.paged_attention_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
                                         self.context_lens, w.scale, self.out, w.max_context_len,
                                         partition_size=self.partition, workspace=self.workspace,
-                                        kv_dtype=self.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+                                        kv_dtype=self.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale,
+                                        shared_blocks=self.shared)
 
     def step(self):
         self.slot_map()

@@ -57,6 +57,23 @@ typedef enum {
   PKV_ERR_LAUNCH = -6       /* the HIP runtime reported an error at launch */
 } pkv_status;
 
+/* Every non-empty decode workspace starts with this many bytes of arrival counters,
+ * which must be zero before the workspace's first use (e.g. hipMemset once after
+ * allocation) and which every paged_attention_decode call leaves zero when it
+ * completes.  Nothing else is ever stored there; the rest of the workspace may hold
+ * anything on entry. */
+#define PKV_WORKSPACE_HEADER_BYTES 32768
+
+/* pkv_cache_desc.flags: the block tables of one decode call may map several
+ * sequences to the same physical block (prefix caching: "La despensa por
+ * casilleros", section "Prefix caching"; "PagedAttention por dentro...", section
+ * "Compartir prefijos").  The decode then reads K/V with the ordinary cache policy,
+ * so a shared block stays in L2 for its other readers.  Without the flag every
+ * K/V byte is assumed to be read once per call and is read with the streaming
+ * (nontemporal) policy, which is faster for such data.  Either way the results are
+ * identical; only speed differs. */
+#define PKV_CACHE_SHARED_BLOCKS 1
+
 /* Describes one layer's paged cache (K and V share it). */
 typedef struct {
   int64_t num_blocks;   /* physical blocks in the pool */
@@ -66,6 +83,7 @@ typedef struct {
   int32_t dtype;        /* pkv_dtype of the stored elements */
   float k_scale;        /* fp8 only: stored code * k_scale = K value (1.0 otherwise) */
   float v_scale;        /* fp8 only: stored code * v_scale = V value */
+  int32_t flags;        /* 0 or PKV_CACHE_SHARED_BLOCKS; other bits: PKV_ERR_SHAPE */
 } pkv_cache_desc;
 
 /*
@@ -103,8 +121,10 @@ int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* 
 /*
  * How paged_attention_decode schedules a call with these arguments.  Returns the
  * schedule (0 = one pass per (sequence, KV head), 1 = fixed partitions merged by a
- * log-sum-exp pass, 2 = balanced: equal shares of 16-token chunks per resident
- * wave, partials merged by a log-sum-exp pass) or a negative pkv_status.
+ * second log-sum-exp kernel, 2 = balanced: one workgroup per CU, equal shares of
+ * 16-token chunks per wave, partial results merged in the same kernel -- through LDS
+ * inside a workgroup, by the last workgroup to finish a context shared between
+ * workgroups) or a negative pkv_status.
  * *partition_out gets the tokens per partition (0 for the balanced schedule),
  * *workers_out the waves of a balanced launch (0 otherwise); either may be NULL.
  * The balanced schedule sizes itself for the current device (a full MI355X when
@@ -141,8 +161,9 @@ size_t paged_attention_workspace_size(const pkv_cache_desc* cache, pkv_dtype q_d
  *                    else tokens per partition, a positive multiple of block_size;
  *                    partial results are merged by a log-sum-exp pass
  *   workspace    : device scratch of >= paged_attention_workspace_size() bytes,
- *                  256-byte aligned (may be NULL when that size is 0); its contents
- *                  on entry do not matter; calls sharing one workspace must not overlap
+ *                  256-byte aligned (may be NULL when that size is 0), whose first
+ *                  PKV_WORKSPACE_HEADER_BYTES are zero (see above); calls sharing one
+ *                  workspace must not overlap (same stream, or synchronised)
  * Supported: head_dim 64 or 128; block_size 16 or 32; group size
  * num_q_heads / num_kv_heads in 1..16; (q, cache) dtypes (f32, f32), (f16, f16),
  * (bf16, bf16), (bf16 or f16, fp8).  Accumulation is fp32; the output is rounded

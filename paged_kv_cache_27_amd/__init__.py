@@ -3,12 +3,12 @@
 The compute runs in libpagedkv.so (hand-written HIP kernels behind the C ABI
 declared in include/pagedkv.h); this package only marshals torch tensors to it.
 """
-from ._binding import (BF16, F16, F32, FP8_E4M3, CacheDesc, PagedKVError, cache_desc,
+from ._binding import (BF16, CACHE_SHARED_BLOCKS, F16, F32, FP8_E4M3, CacheDesc, PagedKVError, cache_desc,
                        load_library, paged_attention_schedule, paged_attention_decode,
                        paged_attention_workspace_size, paged_kv_slot_mapping, paged_kv_write,
-                       pkv_abi_version, pkv_status_string)
+                       pkv_abi_version, pkv_status_string, WORKSPACE_HEADER_BYTES)
 
-__all__ = ["BF16", "F16", "F32", "FP8_E4M3", "CacheDesc", "PagedKVError", "cache_desc",
+__all__ = ["BF16", "CACHE_SHARED_BLOCKS", "F16", "F32", "FP8_E4M3", "CacheDesc", "PagedKVError", "cache_desc",
            "load_library", "paged_attention_schedule", "paged_attention_decode",
            "paged_attention_workspace_size", "paged_kv_slot_mapping", "paged_kv_write",
-           "pkv_abi_version", "pkv_status_string"]
+           "pkv_abi_version", "pkv_status_string", "WORKSPACE_HEADER_BYTES"]

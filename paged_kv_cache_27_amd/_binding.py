@@ -33,7 +33,10 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float)]
+                ("v_scale", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+CACHE_SHARED_BLOCKS = 1  # pkv_cache_desc.flags: blocks may be shared between sequences
 
 
 class PagedKVError(RuntimeError):
@@ -109,16 +112,22 @@ def dtype_code(x) -> int:
 
 
 def cache_desc(k_cache: torch.Tensor, kv_dtype=None, k_scale: float = 1.0,
-               v_scale: float = 1.0) -> CacheDesc:
+               v_scale: float = 1.0, shared_blocks: bool = False) -> CacheDesc:
     """Descriptor of a [num_blocks][H_kv][B][d_h] cache tensor.  An fp8 cache may be a
-    torch.float8_e4m3fn tensor or a uint8 tensor with kv_dtype='fp8'."""
+    torch.float8_e4m3fn tensor or a uint8 tensor with kv_dtype='fp8'.  shared_blocks:
+    the block tables may map several sequences to one physical block (prefix caching)."""
     nb, hkv, bs, d = k_cache.shape
     code = dtype_code(kv_dtype if kv_dtype is not None else k_cache.dtype)
-    return CacheDesc(nb, bs, hkv, d, code, float(k_scale), float(v_scale))
+    return CacheDesc(nb, bs, hkv, d, code, float(k_scale), float(v_scale),
+                     CACHE_SHARED_BLOCKS if shared_blocks else 0)
 
 
 def pkv_status_string(status: int) -> str:
     return load_library().pkv_status_string(status).decode()
+
+
+# Size of the zero-filled counter header at the start of every decode workspace.
+WORKSPACE_HEADER_BYTES = 32768
 
 
 def pkv_abi_version() -> int:
@@ -178,16 +187,19 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            scale: float, out: torch.Tensor, max_context_len: int,
                            partition_size: int = 0, workspace: torch.Tensor | None = None,
                            kv_dtype=None, k_scale: float = 1.0, v_scale: float = 1.0,
-                           q_dtype=None, out_dtype=None, stream=None) -> torch.Tensor:
-    """Decode attention into `out`.  `workspace` (a byte tensor) is allocated here by torch
-    when the call needs one and none is given."""
+                           q_dtype=None, out_dtype=None, shared_blocks: bool = False,
+                           stream=None) -> torch.Tensor:
+    """Decode attention into `out`.  `workspace` (a byte tensor whose first
+    WORKSPACE_HEADER_BYTES are zero, as a fresh torch.zeros tensor is; every call leaves
+    them zero) is allocated here by torch when the call needs one and none is given.
+    shared_blocks: see cache_desc."""
     lib = load_library()
-    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale, shared_blocks)
     n, hq, d = q.shape
     qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
     need = paged_attention_workspace_size(desc, qd, n, hq, max_context_len, partition_size)
     if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     _check("paged_attention_decode",
            lib.paged_attention_decode(

@@ -12,6 +12,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool known_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
 
+// Streaming K/V loads unless the caller says blocks are shared between sequences.
+bool kv_stream(const pkv_cache_desc* c) { return (c->flags & PKV_CACHE_SHARED_BLOCKS) == 0; }
+
 int check_cache(const pkv_cache_desc* c) {
   if (!c) return PKV_ERR_NULL;
   if (!known_dtype(c->dtype)) return PKV_ERR_DTYPE;
@@ -19,6 +22,7 @@ int check_cache(const pkv_cache_desc* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_SHAPE;
   if (c->num_kv_heads <= 0 || c->num_blocks <= 0) return PKV_ERR_SHAPE;
   if (c->dtype == PKV_FP8_E4M3 && !(c->k_scale > 0.0f && c->v_scale > 0.0f)) return PKV_ERR_SHAPE;
+  if (c->flags & ~PKV_CACHE_SHARED_BLOCKS) return PKV_ERR_SHAPE;
   return PKV_OK;
 }
 
@@ -59,14 +63,14 @@ int plan_decode(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
                 int32_t max_context_len, int32_t requested, Plan* out) {
   const int32_t bs = c->block_size;
   const int32_t G = num_q_heads / c->num_kv_heads;
-  if (requested == 0 && num_seqs <= pkv::kStreamKMaxSeqs) {
-    const int w = pkv::streamk_workers(c->dtype, q_dtype, c->head_dim, G, num_seqs);
-    if (w <= 0) return PKV_ERR_DTYPE;
+  pkv::SkPlan sk;
+  if (requested == 0 && num_seqs <= pkv::kStreamKMaxSeqs &&
+      pkv::streamk_plan(c->dtype, q_dtype, c->head_dim, G, num_seqs, kv_stream(c), &sk) == 0) {
     out->mode = kBalanced;
     out->partition = 0;
     out->parts = 0;
-    out->workers = w;
-    out->ws_bytes = pkv::streamk_ws_bytes(num_seqs, G, c->head_dim, w);
+    out->workers = sk.waves;
+    out->ws_bytes = sk.ws_bytes;
     return PKV_OK;
   }
   int32_t p;
@@ -100,7 +104,7 @@ int plan_decode(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 2; }
+int32_t pkv_abi_version(void) { return 3; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -217,6 +221,7 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
   a.v_cache = v_cache;
   a.k_scale = cache->k_scale;
   a.v_scale = cache->v_scale;
+  a.kv_stream = kv_stream(cache) ? 1 : 0;
   a.block_tables = block_tables;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.context_lens = context_lens;
@@ -228,16 +233,17 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
   a.num_partitions = plan.parts;
   a.ws_m = a.ws_l = a.ws_acc = nullptr;
   a.sk_workers = plan.workers;
-  a.sk_cum = nullptr;
+  a.sk_count = nullptr;
   a.sk_part = nullptr;
+  char* body = (char*)workspace + pkv::kWsHeaderBytes;  // only used when ws_bytes > 0
   if (plan.mode == kFixed) {
     const size_t ml = pkv::ws_ml_bytes(num_seqs, num_q_heads, plan.parts);
-    a.ws_m = (float*)workspace;
-    a.ws_l = (float*)((char*)workspace + ml);
-    a.ws_acc = (float*)((char*)workspace + 2 * ml);
+    a.ws_m = (float*)body;
+    a.ws_l = (float*)(body + ml);
+    a.ws_acc = (float*)(body + 2 * ml);
   } else if (plan.mode == kBalanced) {
-    a.sk_cum = (int32_t*)workspace;
-    a.sk_part = (float*)((char*)workspace + pkv::align256((size_t)(num_seqs + 1) * sizeof(int)));
+    a.sk_count = (int32_t*)workspace;
+    a.sk_part = (float*)body;
   }
   hipError_t e = plan.mode == kBalanced ? pkv::launch_decode_streamk(a, stream)
                                         : pkv::launch_decode(a, stream);

@@ -20,10 +20,10 @@
 
 namespace pkv {
 
-template <int KV, int Q, int D, int GP, int NW>
+template <int KV, int Q, int D, int GP, int NW, bool NT>
 __global__ void __launch_bounds__(64 * NW)
 decode_kernel(const DecodeArgs a) {
-  using W = Decoder<KV, Q, D, GP>;
+  using W = Decoder<KV, Q, D, GP, NT>;
 
   __shared__ float lds_p[NW][16 * GP];
   __shared__ float lds_alpha[NW][GP];
@@ -112,7 +112,10 @@ constexpr int kWaves = 4;
 template <int KV, int Q, int D, int GP>
 static hipError_t launch_gp(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<KV, Q, D, GP, kWaves>), grid, dim3(64 * kWaves), 0, stream, a);
+  if (a.kv_stream)
+    hipLaunchKernelGGL((decode_kernel<KV, Q, D, GP, kWaves, true>), grid, dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<KV, Q, D, GP, kWaves, false>), grid, dim3(64 * kWaves), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   hipLaunchKernelGGL((merge_kernel<D, KV>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,

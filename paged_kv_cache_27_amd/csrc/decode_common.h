@@ -156,16 +156,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int KV> struct VFrag {
   static constexpr int W = 2 * DtInfo<KV>::bytes;  // 32-bit words
   uint32_t w[W];
-  __device__ __forceinline__ void load(const uint8_t* p) {
+  template <bool NT>
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off) {
     if constexpr (W == 8) {
-      uint4 a = *(const uint4*)p, b = *(const uint4*)(p + 16);
+      uint4 a = load_kv16<NT>(r, off), b = load_kv16<NT>(r, off + 16);
       w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
       w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     } else if constexpr (W == 4) {
-      uint4 a = *(const uint4*)p;
+      uint4 a = load_kv16<NT>(r, off);
       w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     } else {
-      uint2 a = *(const uint2*)p;
+      uint2 a = load_kv8<NT>(r, off);
       w[0] = a.x; w[1] = a.y;
     }
   }
@@ -184,10 +185,11 @@ template <int KV, int D> struct ChunkRegs {
 
 
 // ============================ fp32: VALU P.V ======================================
-template <int KV, int Q, int D, int GP>
+template <int KV, int Q, int D, int GP, bool NT>
 struct ValuDecoder {
   using T = Qk<KV, Q>;
   using R = ChunkRegs<KV, D>;
+  static constexpr int kDepth = 1;  // chunks whose loads are in flight ahead of the one computed
   static constexpr int EB = DtInfo<KV>::bytes;
   static constexpr int ROW = R::ROW, NC = R::NC, LPR = R::LPR, RPI = R::RPI, NV = R::NV;
   static constexpr int QB = DtInfo<Q>::bytes;
@@ -254,17 +256,18 @@ struct ValuDecoder {
     return ((const __attribute__((address_space(4))) int32_t*)pu)[idx];
   }
 
-  __device__ __forceinline__ void load_chunk(int ct, int blk, R& buf) {
+  // live == false: a padding step past the range's end; its loads read nothing.
+  __device__ __forceinline__ void load_chunk(int ct, int blk, R& buf, bool live) {
     const int lb = ct / BS;
     const size_t tile = (((size_t)blk * Hkv + g) * BS + (ct - lb * BS)) * ROW;
-    const uint8_t* kt = kc + tile;
-    const uint8_t* vt = vc + tile;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + tile, live ? 16 * ROW : 0);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + tile, live ? 16 * ROW : 0);
 #pragma unroll
     for (int c2 = 0; c2 < NC; ++c2)
-      buf.k[c2] = *(const uint4*)(kt + (lane & 15) * ROW + 64 * c2 + 16 * grp);
+      buf.k[c2] = load_kv16<NT>(kr, (lane & 15) * ROW + 64 * c2 + 16 * grp);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      buf.v[i].load(vt + (i * RPI + lane / LPR) * ROW + (lane % LPR) * 8 * EB);
+      buf.v[i].template load<NT>(vr, (i * RPI + lane / LPR) * ROW + (lane % LPR) * 8 * EB);
   }
 
   __device__ __forceinline__ void process_chunk(int ct, const R& buf) {
@@ -464,11 +467,14 @@ template <int KV, int D> struct MfmaChunk {
   uint32_t v[4][VW];
 };
 
-template <int KV, int Q, int D, int GP>
+template <int KV, int Q, int D, int GP, bool NT>
 struct MfmaDecoder {
   using T = Qk<KV, Q>;
   using P = Pv<KV>;
   using Buf = MfmaChunk<KV, D>;
+  // Chunks whose loads are in flight ahead of the one computed.  An fp8 chunk is half
+  // the bytes of a 16-bit one, so it keeps three ahead to hold as many bytes in flight.
+  static constexpr int kDepth = KV == kFP8 ? 3 : 1;
   static constexpr int EB = DtInfo<KV>::bytes;
   static constexpr int ROW = Buf::ROW, NC = Buf::NC, VW = Buf::VW, VBYTES = Buf::VBYTES;
   static constexpr int QB = DtInfo<Q>::bytes;
@@ -527,26 +533,27 @@ struct MfmaDecoder {
     return ((const __attribute__((address_space(4))) int32_t*)pu)[idx];
   }
 
-  __device__ __forceinline__ void load_chunk(int ct, int blk, Buf& buf) {
+  // live == false: a padding step past the range's end; its loads read nothing.
+  __device__ __forceinline__ void load_chunk(int ct, int blk, Buf& buf, bool live) {
     const int lb = ct / BS;
     const size_t tile = (((size_t)blk * Hkv + g) * BS + (ct - lb * BS)) * ROW;
-    const uint8_t* kt = kc + tile;
-    const uint8_t* vt = vc + tile;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + tile, live ? 16 * ROW : 0);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + tile, live ? 16 * ROW : 0);
     const int krow = 4 * (lane & 3) + ((lane & 15) >> 2);  // A-operand row l%16 -> token
 #pragma unroll
     for (int c2 = 0; c2 < NC; ++c2)
-      buf.k[c2] = *(const uint4*)(kt + krow * ROW + 64 * c2 + 16 * (lane >> 4));
+      buf.k[c2] = load_kv16<NT>(kr, krow * ROW + 64 * c2 + 16 * (lane >> 4));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint8_t* p = vt + (4 * k + (lane >> 4)) * ROW + (lane & 15) * VBYTES;
+      const int off = (4 * k + (lane >> 4)) * ROW + (lane & 15) * VBYTES;
       if constexpr (VW == 4) {
-        const uint4 x = *(const uint4*)p;
+        const uint4 x = load_kv16<NT>(vr, off);
         buf.v[k][0] = x.x; buf.v[k][1] = x.y; buf.v[k][2] = x.z; buf.v[k][3] = x.w;
       } else if constexpr (VW == 2) {
-        const uint2 x = *(const uint2*)p;
+        const uint2 x = load_kv8<NT>(vr, off);
         buf.v[k][0] = x.x; buf.v[k][1] = x.y;
       } else {
-        buf.v[k][0] = *(const uint32_t*)p;
+        buf.v[k][0] = load_kv4<NT>(vr, off);
       }
     }
   }
@@ -658,22 +665,20 @@ struct MfmaDecoder {
   }
 };
 
-template <int KV, int Q, int D, int GP>
-using Decoder = typename std::conditional<KV == kF32, ValuDecoder<KV, Q, D, GP>,
-                                          MfmaDecoder<KV, Q, D, GP>>::type;
+template <int KV, int Q, int D, int GP, bool NT>
+using Decoder = typename std::conditional<KV == kF32, ValuDecoder<KV, Q, D, GP, NT>,
+                                          MfmaDecoder<KV, Q, D, GP, NT>>::type;
 
 // Chunks c_begin, c_begin + step, ... < c_end (chunk c covers tokens 16c .. 16c+15),
-// with the loads of the next DEPTH chunks in flight while one is computed (DEPTH + 1
-// register buffers, rotated by a fully unrolled inner loop).  Every step issues the
-// same loads unconditionally -- near the end it re-reads the last chunk, which is in
-// cache -- so the vector-memory wait before a chunk's use only covers that chunk's
-// own loads, never the ones issued after it.  Block-table entries come one chunk
-// ahead through the scalar path.
-#ifndef PKV_PIPE_DEPTH
-#define PKV_PIPE_DEPTH 1
-#endif
-template <int DEPTH = PKV_PIPE_DEPTH, class W>
+// with the loads of the next W::kDepth chunks in flight while one is computed
+// (kDepth + 1 register buffers, rotated by a fully unrolled inner loop).  Every step
+// issues its loads unconditionally -- past the end as padding loads through an empty
+// buffer resource, which read nothing -- so the vector-memory wait before a chunk's
+// use only covers that chunk's own loads, never the ones issued after it.
+// Block-table entries come one chunk ahead through the scalar path.
+template <class W>
 __device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int step) {
+  constexpr int DEPTH = W::kDepth;
   if (c_begin >= c_end) return;
   const int n = (c_end - c_begin + step - 1) / step;  // chunks of this wave
   auto chunk = [&](int i) { return c_begin + (i < n ? i : n - 1) * step; };
@@ -681,7 +686,7 @@ __device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int st
   int blk = wd.table_entry(chunk(0));
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) {
-    wd.load_chunk(16 * chunk(j), blk, buf[j]);
+    wd.load_chunk(16 * chunk(j), blk, buf[j], j < n);
     blk = wd.table_entry(chunk(j + 1));
   }
   for (int i = 0; i < n; i += DEPTH + 1) {
@@ -689,7 +694,7 @@ __device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int st
     for (int u = 0; u <= DEPTH; ++u) {
       const int ii = i + u;
       if (ii >= n) break;
-      wd.load_chunk(16 * chunk(ii + DEPTH), blk, buf[(u + DEPTH) % (DEPTH + 1)]);
+      wd.load_chunk(16 * chunk(ii + DEPTH), blk, buf[(u + DEPTH) % (DEPTH + 1)], ii + DEPTH < n);
       blk = wd.table_entry(chunk(ii + DEPTH + 1));
       wd.process_chunk(16 * chunk(ii), buf[u]);
     }

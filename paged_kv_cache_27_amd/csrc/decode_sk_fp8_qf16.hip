@@ -1,0 +1,9 @@
+// Instantiations of the balanced decode kernel for fp8 caches with f16 queries.
+#define PKV_SK_DEFINE
+#include "decode_sk_kernel.h"
+
+namespace pkv {
+
+PKV_SK_FOR_DTYPES(PKV_SK_INSTANTIATE, kFP8, kF16)
+
+}  // namespace pkv

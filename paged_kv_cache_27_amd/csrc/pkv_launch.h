@@ -28,6 +28,7 @@ struct DecodeArgs {
   const void* k_cache;
   const void* v_cache;
   float k_scale, v_scale;
+  int32_t kv_stream;       // 1: K/V read with the streaming (nontemporal) policy
   const int32_t* block_tables;
   int32_t max_blocks_per_seq;
   const int32_t* context_lens;
@@ -42,8 +43,8 @@ struct DecodeArgs {
   float* ws_acc;           // [N][H_q][P][D] unnormalised outputs
   // balanced schedule
   int32_t sk_workers;      // waves in the launch
-  int32_t* sk_cum;         // [N + 1] chunk prefix, written by the decode kernel
-  float* sk_part;          // [2 * workers][2 * GP + GP * D] partials
+  int32_t* sk_count;       // [workgroups] arrival counters: zero on entry, zero on exit
+  float* sk_part;          // [2 * workgroups] partials: m[GP], l[GP], (16-byte aligned) acc[GP][D]
 };
 
 hipError_t launch_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t n,
@@ -54,21 +55,32 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);          // fixed partitions
 hipError_t launch_decode_streamk(const DecodeArgs& a, hipStream_t stream);  // balanced
 
-// Balanced schedule: resident waves of the chosen kernel on the current device (a
-// full MI355X if no device is visible), 0 for an unsupported combination; and the
-// workspace it needs.  The sequence count is capped by the LDS prefix array.
+// Balanced schedule: one workgroup per resident slot of the chosen kernel on the
+// current device (a full MI355X if no device is visible).  streamk_plan fills the
+// waves of the launch and the workspace it needs; it returns 0, or -1 for an
+// unsupported combination or a kernel that does not fit a CU (e.g. too many sequences
+// for its LDS prefix array).
 constexpr int kStreamKMaxSeqs = 8191;
+constexpr int kStreamKMaxGroups = 8192;
+struct SkPlan {
+  int waves;
+  size_t ws_bytes;
+};
 int pad_group(int G);
-int streamk_workers(int cache_dtype, int q_dtype, int head_dim, int group, int num_seqs);
-size_t streamk_ws_bytes(int num_seqs, int group, int head_dim, int workers);
+int streamk_plan(int cache_dtype, int q_dtype, int head_dim, int group, int num_seqs, bool kv_stream,
+                 SkPlan* out);
 
-// Workspace layout for split mode, each array 256-byte aligned.
+// Every workspace starts with a header of arrival counters (one int per workgroup of
+// a balanced launch) that is zero before the first call and that every call leaves
+// zero; no schedule stores anything else there.  Arrays after it are 256-byte aligned.
+constexpr size_t kWsHeaderBytes = (size_t)kStreamKMaxGroups * sizeof(int32_t);
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t ws_ml_bytes(int64_t n, int64_t hq, int64_t parts) {
   return align256((size_t)(n * hq * parts) * sizeof(float));
 }
 inline size_t ws_total_bytes(int64_t n, int64_t hq, int64_t d, int64_t parts) {
-  return 2 * ws_ml_bytes(n, hq, parts) + align256((size_t)(n * hq * parts * d) * sizeof(float));
+  return kWsHeaderBytes + 2 * ws_ml_bytes(n, hq, parts) +
+         align256((size_t)(n * hq * parts * d) * sizeof(float));
 }
 
 }  // namespace pkv

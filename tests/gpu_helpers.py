@@ -84,14 +84,18 @@ class GpuStep:
         pkv.paged_kv_write(self.new_slots, self.new_k, self.new_v, self.k_cache, self.v_cache,
                            self.kv_dtype, w.k_scale, w.v_scale)
 
-    def decode(self, partition_size=None, out=None, workspace=None):
+    def decode(self, partition_size=None, out=None, workspace=None, shared_blocks=None):
+        """shared_blocks: the cache-policy flag; by default set when the workload maps
+        several sequences to one physical block."""
         w, c = self.w, self.w.cfg
         part = c.partition_size if partition_size is None else partition_size
         out = self.out if out is None else out
+        shared = bool(w.shared_blocks) if shared_blocks is None else shared_blocks
         pkv.paged_attention_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
                                    self.context_lens, w.scale, out, w.max_context_len,
                                    partition_size=part, workspace=workspace,
-                                   kv_dtype=self.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+                                   kv_dtype=self.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale,
+                                   shared_blocks=shared)
         return out
 
     def run(self, partition_size=None):

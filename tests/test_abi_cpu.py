@@ -26,7 +26,12 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pkv.pkv_abi_version() == 2
+    assert pkv.pkv_abi_version() == 3
+
+
+def test_workspace_header_constant_matches_header():
+    m = re.search(r"#define\s+PKV_WORKSPACE_HEADER_BYTES\s+(\d+)", HEADER.read_text())
+    assert m and int(m.group(1)) == pkv.WORKSPACE_HEADER_BYTES
 
 
 def test_status_strings():
@@ -57,6 +62,8 @@ def test_decode_argument_errors():
     assert _decode(lib, _desc(), q_dtype=pkv.F16) == -2  # q dtype != cache dtype
     assert _decode(lib, _desc(dtype=pkv.FP8_E4M3), q_dtype=pkv.F32) == -2
     assert _decode(lib, _desc(dtype=7)) == -2
+    assert _decode(lib, _desc(flags=2)) == -3  # unknown cache flag
+    assert _decode(lib, _desc(flags=pkv.CACHE_SHARED_BLOCKS), n=0) == 0
     assert _decode(lib, _desc(dtype=pkv.FP8_E4M3, k_scale=0.0), q_dtype=pkv.BF16) == -3
     assert _decode(lib, _desc(), out_dtype=pkv.FP8_E4M3) == -2
     assert _decode(lib, _desc(), q=None) == -1
@@ -80,10 +87,15 @@ def test_workspace_sizes_and_schedules():
     sch = pkv.paged_attention_schedule(d, pkv.BF16, 8, 32, 32768, 512)
     assert sch == {"schedule": "fixed-partitions", "partition": 512, "workers": 0}
     sch = pkv.paged_attention_schedule(d, pkv.BF16, 64, 32, 4096, 0)
-    assert sch["schedule"] == "balanced" and sch["workers"] > 0 and sch["workers"] % 4 == 0
-    # balanced: chunk prefix (N+1 ints) and two partials per wave (m, l, acc for 4 heads)
+    # balanced, 4 query heads per KV head: workgroups of 8 waves, one per CU
+    assert sch["schedule"] == "balanced" and sch["workers"] > 0 and sch["workers"] % 8 == 0
+    # the counter header, then two partials per workgroup (m, l, acc for 4 heads)
     ws = pkv.paged_attention_workspace_size(d, pkv.BF16, 64, 32, 4096, 0)
-    assert ws >= 2 * sch["workers"] * (2 * 4 + 4 * 128) * 4
+    assert ws >= pkv.WORKSPACE_HEADER_BYTES + 2 * (sch["workers"] // 8) * (2 * 4 + 4 * 128) * 4
+    assert sch["workers"] // 8 * 4 <= pkv.WORKSPACE_HEADER_BYTES  # one counter per workgroup
+    # fixed partitions keep the header clear too
+    assert pkv.paged_attention_workspace_size(d, pkv.BF16, 8, 32, 32768, 512) >= (
+        pkv.WORKSPACE_HEADER_BYTES + 8 * 32 * 64 * (128 + 2) * 4)
     assert pkv.paged_attention_schedule(d, pkv.BF16, 8, 32, 300, -1)["schedule"] == "single-pass"
     assert pkv.paged_attention_schedule(d, pkv.BF16, 9000, 32, 3000, 0)["schedule"] == "fixed-partitions"
     with pytest.raises(pkv.PagedKVError):
@@ -119,3 +131,14 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         pkv.paged_kv_slot_mapping(t, t, torch.zeros((1, 4), dtype=torch.int32), 16,
                                   slot_mapping=torch.zeros(4, dtype=torch.int64))
+
+
+def test_even_split_owner_formula():
+    """The balanced kernel splits T units into P parts, part p = [T p / P, T (p+1) / P),
+    and finds the part holding unit x as ((x + 1) P - 1) / T (integer division); both
+    levels (workgroups, then waves) rely on that inverse for T >= P >= 1."""
+    for T in range(1, 260):
+        for P in range(1, min(T, 40) + 1):
+            for p in range(P):
+                for x in range(T * p // P, T * (p + 1) // P):
+                    assert ((x + 1) * P - 1) // T == p, (T, P, x)

@@ -169,6 +169,42 @@ def test_split_matches_single():
         assert (split - single).abs().max().item() <= 1e-5, part
 
 
+@pytest.mark.parametrize("name", ["prefix", "r70b", "llama8b"])
+def test_cache_policy_flag_bit_identical(name):
+    """The shared-blocks flag only changes the load cache policy: outputs are bit-identical
+    with and without it, in every schedule."""
+    w = make_workload(SMALL[name])
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    for part in (0, -1, 2 * w.cfg.block_size):
+        a = g.decode(part, shared_blocks=False).clone()
+        b = g.decode(part, shared_blocks=True).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (name, part)
+
+
+def test_workspace_reuse_keeps_header_zero():
+    """One workspace serves balanced, fixed and balanced-again calls of different shapes:
+    results match a fresh workspace each time and the counter header is zero after every
+    call (the balanced kernel's arrival counters return to zero)."""
+    hdr = pkv.WORKSPACE_HEADER_BYTES
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for n, lo, hi, part in ((6, 300, 1700, 0), (40, 16, 4000, 0), (5, 100, 900, 64), (17, 1, 2500, 0),
+                            (3, 9000, 12000, 0)):
+        cfg = LLAMA8B.replace(num_seqs=n, ctx_params=(lo, hi), out_dtype="f32")
+        g = GpuStep(make_workload(cfg))
+        g.fill_history()
+        g.write_new()
+        for rep in range(3):
+            got = g.decode(part, workspace=ws).clone()
+            torch.cuda.synchronize()
+            assert int(ws[:hdr].count_nonzero().item()) == 0, (n, part, rep)
+            ref = g.decode(part).clone()  # fresh zeroed workspace from the binding
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref), (n, part, rep)
+
+
 # ------------------------------------------------------------- edge cases --------
 EDGE = {
     "ctx-edges-b16": LLAMA8B.replace(num_seqs=9, ctx_kind="fixed",
