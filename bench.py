@@ -30,9 +30,11 @@ if str(ROOT) not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective KV GB/s (% of HBM peak) and seq-heads/s per decode layer"
 DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
-KERNEL_SOURCES = ["paged_kv_cache_27_amd/csrc/decode.hip", "paged_kv_cache_27_amd/csrc/decode_sk.hip",
-                  "paged_kv_cache_27_amd/csrc/decode_common.h", "paged_kv_cache_27_amd/csrc/pkv_device.h",
-                  "paged_kv_cache_27_amd/csrc/pkv_launch.h", "paged_kv_cache_27_amd/csrc/api.cpp"]
+CSRC = "paged_kv_cache_27_amd/csrc"
+KERNEL_SOURCES = [f"{CSRC}/{n}" for n in (
+    "decode.hip", "decode_sk.hip", "decode_sk_kernel.h", "decode_sk_bf16.hip", "decode_sk_f16.hip",
+    "decode_sk_f32.hip", "decode_sk_fp8_qbf16.hip", "decode_sk_fp8_qf16.hip", "decode_common.h",
+    "pkv_device.h", "pkv_launch.h", "api.cpp")]
 
 
 def log(*a):
@@ -165,7 +167,7 @@ class Step:
 
 
 KERNEL_LABEL = {
-    "balanced": "paged_attention_decode call (decode_sk_kernel + merge_sk_kernel)",
+    "balanced": "paged_attention_decode call (decode_sk_kernel, merges in-kernel)",
     "fixed-partitions": "paged_attention_decode call (decode_kernel + merge_kernel)",
     "single-pass": "paged_attention_decode call (decode_kernel)",
 }

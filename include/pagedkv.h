@@ -11,9 +11,10 @@
  *
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer owned by the caller (allocated by
- *     any HIP allocator, e.g. PyTorch).  The library allocates and frees nothing
- *     and keeps no global mutable state; concurrent calls on different streams
- *     are safe as long as they do not write the same memory.
+ *     any HIP allocator, e.g. PyTorch).  The library allocates and frees nothing;
+ *     its only global state is a per-device cache of kernel-occupancy queries
+ *     (filled on first use, safe under concurrent calls).  Concurrent calls on
+ *     different streams are safe as long as they do not write the same memory.
  *   - Every call is asynchronous on `stream` (NULL = the null stream).  Buffers
  *     must stay alive until the caller synchronises.  Host-visible argument
  *     errors are returned before anything is launched; no call synchronises

@@ -197,9 +197,11 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale, shared_blocks)
     n, hq, d = q.shape
     qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
-    need = paged_attention_workspace_size(desc, qd, n, hq, max_context_len, partition_size)
-    if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = paged_attention_workspace_size(desc, qd, n, hq, max_context_len, partition_size)
+        if need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    # a workspace that is too small is refused by the library (PKV_ERR_WORKSPACE)
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     _check("paged_attention_decode",
            lib.paged_attention_decode(
@@ -207,6 +209,6 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
                block_tables.shape[1], _ptr(context_lens), int(max_context_len), float(scale),
                _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
-               int(partition_size), _ptr(workspace) if need else None,
-               workspace.numel() if need else 0, _stream(stream)))
+               int(partition_size), _ptr(workspace) if workspace is not None else None,
+               workspace.numel() if workspace is not None else 0, _stream(stream)))
     return out

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "decode_sk_kernel.h"
 
 namespace pkv {
@@ -51,6 +53,17 @@ int pad_group(int G) {
   return gp;
 }
 
+// Occupancy of each balanced-kernel instantiation, cached per device: the query is a
+// pure function of (device, kernel, LDS bytes) and costs microseconds of host time per
+// call otherwise.  Entries are filled once, racing writers store the same value.
+namespace {
+constexpr int kMaxDevices = 64;
+constexpr int kCacheSlots = 5 * 5 * 2 * 5 * 2;  // cache dtype x q dtype x head dim x group x policy
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_per_cu[kMaxDevices][kCacheSlots];
+int gp_index(int gp) { return gp == 1 ? 0 : gp == 2 ? 1 : gp == 4 ? 2 : gp == 8 ? 3 : 4; }
+}  // namespace
+
 int streamk_plan(int cache_dtype, int q_dtype, int head_dim, int group, int num_seqs, bool kv_stream,
                  SkPlan* out) {
   const int gp = pad_group(group);
@@ -58,12 +71,30 @@ int streamk_plan(int cache_dtype, int q_dtype, int head_dim, int group, int num_
   hipError_t e = with_sk(cache_dtype, q_dtype, head_dim, gp, kv_stream, [&](auto k) {
     using K = decltype(k);
     int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K::decode(), 64 * K::NW, lds) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
       (void)hipGetLastError();
       cus = 256;  // no device visible (host-only use): size for a full MI355X
       per_cu = 1;
+    } else {
+      const bool cacheable = dev < kMaxDevices && cache_dtype >= 0 && cache_dtype < 5 && q_dtype >= 0 &&
+                             q_dtype < 5 && lds <= 4096;  // small LDS requests share one entry
+      const int slot = (((cache_dtype * 5 + q_dtype) * 2 + (head_dim == 128)) * 5 + gp_index(gp)) * 2 + kv_stream;
+      if (cacheable) {
+        cus = g_cus[dev].load(std::memory_order_relaxed);
+        per_cu = g_per_cu[dev][slot].load(std::memory_order_relaxed);
+      }
+      if (cus <= 0 || per_cu <= 0) {
+        const size_t lds_q = cacheable ? 4096 : lds;  // a cached entry must hold for any small N
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K::decode(), 64 * K::NW, lds_q) != hipSuccess) {
+          (void)hipGetLastError();
+          cus = 256;
+          per_cu = 1;
+        } else if (cacheable && cus > 0 && per_cu > 0) {
+          g_cus[dev].store(cus, std::memory_order_relaxed);
+          g_per_cu[dev][slot].store(per_cu, std::memory_order_relaxed);
+        }
+      }
     }
     if (cus <= 0 || per_cu <= 0) return hipErrorInvalidValue;  // does not fit a CU
     const int wgs = cus * per_cu < kStreamKMaxGroups ? cus * per_cu : kStreamKMaxGroups;
