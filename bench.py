@@ -33,6 +33,7 @@ DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 CSRC = "paged_kv_cache_27_amd/csrc"
 KERNEL_SOURCES = [f"{CSRC}/{n}" for n in (
     "decode.hip", "decode_sk.hip", "decode_sk_kernel.h", "decode_sk_bf16.hip", "decode_sk_f16.hip",
+    "decode_sk_pre.hip", "prefix.hip",
     "decode_sk_f32.hip", "decode_sk_fp8_qbf16.hip", "decode_sk_fp8_qf16.hip", "decode_common.h",
     "pkv_device.h", "pkv_launch.h", "api.cpp")]
 
@@ -54,6 +55,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the oracle leg")
     ap.add_argument("--partition", type=int, default=None, help="override the partition size")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="prefix-sharing workloads: plain decode instead of the shared-prefix entry point")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy --steps times (counter calibration)")
     return ap.parse_args()
@@ -91,7 +94,7 @@ def algorithmic_bytes(w):
 class Step:
     """Device-resident inputs of one decode step and the three ABI calls that run it."""
 
-    def __init__(self, w, partition=None):
+    def __init__(self, w, partition=None, shared_prefix=True):
         import numpy as np
         import torch
         import paged_kv_cache_27_amd as pkv
@@ -132,6 +135,20 @@ class Step:
                                                      c.num_q_heads, w.max_context_len,
                                                      self.partition)
         self.workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        # Prefix sharing: the shared-prefix entry point with the workload's own grouping
+        # (every group's prefix read once), unless a partition was asked for.
+        self.prefix = None
+        if self.shared and c.ctx_kind == "prefix" and self.partition == 0 and shared_prefix:
+            starts = w.prefix_group_starts()
+            plens = np.full(c.num_seqs, int(c.ctx_params[0]), np.int32)
+            gmax, pmax = int(np.diff(starts).max()), int(plens.max())
+            self.prefix = (torch.from_numpy(starts).to(dev), torch.from_numpy(plens).to(dev), gmax, pmax)
+            pneed = pkv.paged_attention_shared_prefix_workspace_size(
+                self.desc, c.q_dtype, c.num_seqs, c.num_q_heads, w.max_context_len, len(starts) - 1,
+                gmax, pmax)
+            self.pworkspace = torch.zeros(pneed, dtype=torch.uint8, device=dev)
+            self.schedule = {"schedule": "shared-prefix", "partition": 0,
+                             "workers": self.schedule.get("workers", 0), "groups": len(starts) - 1}
         # history: every cached token written once through the same write kernel
         if w.hist_seq.size:
             hs = torch.from_numpy(w.hist_seq).to(dev)
@@ -154,6 +171,12 @@ class Step:
 
     def decode(self):
         w = self.w
+        if self.prefix is not None:
+            starts, plens, gmax, pmax = self.prefix
+            self.pkv.paged_attention_decode_shared_prefix(
+                self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, w.scale,
+                self.out, w.max_context_len, starts, plens, gmax, pmax, workspace=self.pworkspace)
+            return
         self.pkv.paged_attention_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
                                         self.context_lens, w.scale, self.out, w.max_context_len,
                                         partition_size=self.partition, workspace=self.workspace,
@@ -170,6 +193,7 @@ KERNEL_LABEL = {
     "balanced": "paged_attention_decode call (decode_sk_kernel, merges in-kernel)",
     "fixed-partitions": "paged_attention_decode call (decode_kernel + merge_kernel)",
     "single-pass": "paged_attention_decode call (decode_kernel)",
+    "shared-prefix": "paged_attention_decode_shared_prefix call (prefix_kernel + decode_sk_kernel suffix pass)",
 }
 
 
@@ -197,7 +221,8 @@ def measure(cfg, args, partition=None):
     t0 = time.time()
     w = make_workload(cfg)
     log(f"[{cfg.name}] inputs generated in {time.time() - t0:.1f}s")
-    st = Step(w, partition if partition is not None else args.partition)
+    st = Step(w, partition if partition is not None else args.partition,
+              shared_prefix=not args.no_shared_prefix)
     nbytes = algorithmic_bytes(w)
 
     for _ in range(args.warmup):

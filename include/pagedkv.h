@@ -180,6 +180,51 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
                            pkv_dtype out_dtype, int32_t partition_size, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Decode attention for a batch in which groups of sequences share a prefix of physical
+ * blocks -- prefix caching: their block tables point at the same refcounted blocks
+ * ("La despensa por casilleros", section "Prefix caching: compartir casilleros con
+ * copy-on-write"; "PagedAttention por dentro...", section "Compartir prefijos").
+ * Computes exactly what paged_attention_decode computes (same contract for every
+ * argument it shares with it), reading each group's shared prefix once for the whole
+ * group instead of once per sequence: the queries of the group's sequences are stacked
+ * as the rows of one matrix product over the prefix tokens (on the matrix cores), each
+ * sequence's remaining tokens are streamed as by the balanced schedule, and the two
+ * partial softmax results are merged with the log-sum-exp algebra ("Optimizacion de
+ * Inferencia LLM", section "PagedAttention: Conceptos de SO..."; online softmax).
+ *   group_starts   : int32 [num_groups + 1], ascending, group_starts[0] = 0,
+ *                    group_starts[num_groups] = num_seqs; group j is sequences
+ *                    group_starts[j] .. group_starts[j+1] - 1
+ *   num_groups     : >= 1 (<= num_seqs); a sequence that shares nothing may be a
+ *                    group of its own with prefix length 0
+ *   max_group_size : host-side upper bound of the group sizes (sizes the grid)
+ *   prefix_lens    : int32 [num_seqs]; the first prefix_lens[s] tokens of sequence s
+ *                    lie in the blocks its group shares: equal for every sequence of a
+ *                    group, a multiple of block_size, <= context_lens[s], and
+ *                    block_tables[s][0 .. prefix_lens[s] / block_size) identical across
+ *                    the group.  0 = nothing shared.
+ *   max_prefix_len : host-side upper bound of prefix_lens (a multiple of block_size)
+ *   workspace      : >= paged_attention_shared_prefix_workspace_size() bytes, 256-byte
+ *                    aligned, first PKV_WORKSPACE_HEADER_BYTES zero (as for
+ *                    paged_attention_decode); never NULL
+ * Supported: the 16-bit caches ((bf16, bf16), (f16, f16)); head_dim, block_size and
+ * group size as for paged_attention_decode; up to 8191 sequences.  Other dtypes
+ * return PKV_ERR_DTYPE.  The grouping only selects the work split: any grouping that
+ * meets the preconditions gives the same attention, to within fp32 rounding order.
+ * Preconditions beyond those of paged_attention_decode are not checked on the device.
+ */
+size_t paged_attention_shared_prefix_workspace_size(const pkv_cache_desc* cache, pkv_dtype q_dtype,
+                                                    int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t max_context_len, int32_t num_groups,
+                                                    int32_t max_group_size, int32_t max_prefix_len);
+int paged_attention_decode_shared_prefix(
+    const void* q, pkv_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+    const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+    const int32_t* group_starts, int32_t num_groups, int32_t max_group_size, const int32_t* prefix_lens,
+    int32_t max_prefix_len, float scale, void* out, pkv_dtype out_dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* pkv_status_string(int status);
 

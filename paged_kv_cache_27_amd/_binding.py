@@ -23,8 +23,9 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHA
           -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH"}
 
 EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_schedule",
-            "paged_attention_workspace_size", "paged_attention_decode", "pkv_status_string",
-            "pkv_abi_version"]
+            "paged_attention_workspace_size", "paged_attention_decode",
+            "paged_attention_shared_prefix_workspace_size", "paged_attention_decode_shared_prefix",
+            "pkv_status_string", "pkv_abi_version"]
 SCHEDULES = {0: "single-pass", 1: "fixed-partitions", 2: "balanced"}
 
 
@@ -73,6 +74,14 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.POINTER(CacheDesc), vp, i32, vp, i32, f32, vp,
                                            ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_shared_prefix_workspace_size.argtypes = [ctypes.POINTER(CacheDesc), ctypes.c_int,
+                                                                 i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_shared_prefix_workspace_size.restype = ctypes.c_size_t
+    lib.paged_attention_decode_shared_prefix.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp,
+                                                         ctypes.POINTER(CacheDesc), vp, i32, vp, i32,
+                                                         vp, i32, i32, vp, i32, f32, vp, ctypes.c_int,
+                                                         vp, ctypes.c_size_t, vp]
+    lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -211,4 +220,45 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
                int(partition_size), _ptr(workspace) if workspace is not None else None,
                workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def paged_attention_shared_prefix_workspace_size(desc: CacheDesc, q_dtype, num_seqs: int,
+                                                 num_q_heads: int, max_context_len: int,
+                                                 num_groups: int, max_group_size: int,
+                                                 max_prefix_len: int) -> int:
+    return int(load_library().paged_attention_shared_prefix_workspace_size(
+        ctypes.byref(desc), dtype_code(q_dtype), num_seqs, num_q_heads, max_context_len, num_groups,
+        max_group_size, max_prefix_len))
+
+
+def paged_attention_decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                         block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                         scale: float, out: torch.Tensor, max_context_len: int,
+                                         group_starts: torch.Tensor, prefix_lens: torch.Tensor,
+                                         max_group_size: int, max_prefix_len: int,
+                                         workspace: torch.Tensor | None = None, q_dtype=None,
+                                         out_dtype=None, stream=None) -> torch.Tensor:
+    """Decode attention into `out` for prefix-sharing groups (see include/pagedkv.h).
+    group_starts: int32 [num_groups + 1]; prefix_lens: int32 [num_seqs].  `workspace`
+    (zero-headed, as for paged_attention_decode) is allocated by torch when not given."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    n, hq, d = q.shape
+    qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
+    ng = group_starts.numel() - 1
+    assert group_starts.dtype == torch.int32 and prefix_lens.dtype == torch.int32
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    if workspace is None:
+        need = paged_attention_shared_prefix_workspace_size(desc, qd, n, hq, max_context_len, ng,
+                                                            max_group_size, max_prefix_len)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check("paged_attention_decode_shared_prefix",
+           lib.paged_attention_decode_shared_prefix(
+               _ptr(q), qd, n, hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+               _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
+               _ptr(group_starts), ng, int(max_group_size), _ptr(prefix_lens), int(max_prefix_len),
+               float(scale), _ptr(out),
+               dtype_code(out_dtype if out_dtype is not None else out.dtype),
+               _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

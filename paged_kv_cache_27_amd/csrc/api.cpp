@@ -65,7 +65,7 @@ int plan_decode(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
   const int32_t G = num_q_heads / c->num_kv_heads;
   pkv::SkPlan sk;
   if (requested == 0 && num_seqs <= pkv::kStreamKMaxSeqs &&
-      pkv::streamk_plan(c->dtype, q_dtype, c->head_dim, G, num_seqs, kv_stream(c), &sk) == 0) {
+      pkv::streamk_plan(c->dtype, q_dtype, c->head_dim, G, num_seqs, kv_stream(c), false, &sk) == 0) {
     out->mode = kBalanced;
     out->partition = 0;
     out->parts = 0;
@@ -97,6 +97,41 @@ int plan_decode(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
     out->parts = (max_context_len + p - 1) / p;
     out->ws_bytes = pkv::ws_total_bytes(num_seqs, num_q_heads, c->head_dim, out->parts);
   }
+  return PKV_OK;
+}
+
+// The shared-prefix decode: prefix partials, then the balanced suffix pass.
+struct PrefixPlan {
+  int32_t splits;       // slices of each prefix's chunks (prefix kernel workgroups per row tile)
+  int32_t tiles;        // 128-row tiles per group
+  size_t part_bytes;    // prefix partials
+  pkv::SkPlan sk;       // suffix pass
+  size_t ws_bytes;
+};
+
+int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
+                int32_t max_prefix_len, PrefixPlan* out) {
+  if (c->dtype != PKV_BF16 && c->dtype != PKV_F16) return PKV_ERR_DTYPE;
+  if (num_groups < 1 || max_group_size < 1 || max_prefix_len < 0) return PKV_ERR_SHAPE;
+  if (max_prefix_len % c->block_size != 0 || max_prefix_len > max_context_len) return PKV_ERR_SHAPE;
+  if (num_seqs > pkv::kStreamKMaxSeqs || num_groups > num_seqs) return PKV_ERR_SHAPE;
+  const int32_t G = num_q_heads / c->num_kv_heads;
+  if (pkv::streamk_plan(c->dtype, q_dtype, c->head_dim, G, num_seqs, true, true, &out->sk) != 0)
+    return PKV_ERR_SHAPE;
+  out->tiles = (int32_t)(((int64_t)max_group_size * G + pkv::kPrefixRows - 1) / pkv::kPrefixRows);
+  // Enough prefix workgroups to cover the CUs once (one per suffix workgroup), at most 8
+  // slices and at most one per 16-token chunk of the longest prefix.
+  const int64_t per_split = (int64_t)num_groups * out->tiles * c->num_kv_heads;
+  const int64_t wgs = out->sk.waves / 8 > 0 ? out->sk.waves / 8 : 1;
+  int64_t splits = (wgs + per_split - 1) / per_split;
+  const int64_t max_splits = max_prefix_len / 16 > 0 ? max_prefix_len / 16 : 1;
+  splits = splits < 1 ? 1 : (splits > 8 ? 8 : splits);
+  splits = splits > max_splits ? max_splits : splits;
+  if (per_split * splits > 0x7fffffff) return PKV_ERR_SHAPE;
+  out->splits = (int32_t)splits;
+  out->part_bytes = pkv::align256((size_t)num_seqs * num_q_heads * splits * (4 + c->head_dim) * sizeof(float));
+  out->ws_bytes = out->sk.ws_bytes + out->part_bytes;
   return PKV_OK;
 }
 
@@ -235,6 +270,9 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
   a.sk_workers = plan.workers;
   a.sk_count = nullptr;
   a.sk_part = nullptr;
+  a.seq_begin = nullptr;
+  a.pre_part = nullptr;
+  a.pre_splits = 0;
   char* body = (char*)workspace + pkv::kWsHeaderBytes;  // only used when ws_bytes > 0
   if (plan.mode == kFixed) {
     const size_t ml = pkv::ws_ml_bytes(num_seqs, num_q_heads, plan.parts);
@@ -247,6 +285,101 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
   }
   hipError_t e = plan.mode == kBalanced ? pkv::launch_decode_streamk(a, stream)
                                         : pkv::launch_decode(a, stream);
+  if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+size_t paged_attention_shared_prefix_workspace_size(const pkv_cache_desc* cache, pkv_dtype q_dtype,
+                                                    int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t max_context_len, int32_t num_groups,
+                                                    int32_t max_group_size, int32_t max_prefix_len) {
+  if (check_decode_shape(cache, q_dtype, q_dtype, num_seqs, num_q_heads, max_context_len)) return 0;
+  if (num_seqs == 0) return 0;
+  PrefixPlan plan;
+  if (plan_prefix(cache, q_dtype, num_seqs, num_q_heads, max_context_len, num_groups, max_group_size,
+                  max_prefix_len, &plan))
+    return 0;
+  return plan.ws_bytes;
+}
+
+int paged_attention_decode_shared_prefix(
+    const void* q, pkv_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+    const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+    const int32_t* group_starts, int32_t num_groups, int32_t max_group_size, const int32_t* prefix_lens,
+    int32_t max_prefix_len, float scale, void* out, pkv_dtype out_dtype, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  int st = check_decode_shape(cache, q_dtype, out_dtype, num_seqs, num_q_heads, max_context_len);
+  if (st) return st;
+  if (max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  PrefixPlan plan;
+  st = plan_prefix(cache, q_dtype, num_seqs, num_q_heads, max_context_len, num_groups, max_group_size,
+                   max_prefix_len, &plan);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !group_starts ||
+      !prefix_lens || !workspace)
+    return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
+  if (workspace_bytes < plan.ws_bytes || ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
+
+  float* pre_part = (float*)((char*)workspace + plan.sk.ws_bytes);
+  if (max_prefix_len > 0) {
+    pkv::PrefixArgs p;
+    p.q = q;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.head_dim = cache->head_dim;
+    p.block_size = cache->block_size;
+    p.cache_dtype = cache->dtype;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.group_starts = group_starts;
+    p.prefix_lens = prefix_lens;
+    p.scale = scale;
+    p.pre_part = pre_part;
+    p.splits = plan.splits;
+    p.tiles = plan.tiles;
+    hipError_t e = pkv::launch_prefix(p, num_groups, stream);
+    if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
+    if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.cache_dtype = cache->dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.kv_stream = 1;  // the suffixes are each sequence's own blocks
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.partition = 0;
+  a.num_partitions = 0;
+  a.ws_m = a.ws_l = a.ws_acc = nullptr;
+  a.sk_workers = plan.sk.waves;
+  a.sk_count = (int32_t*)workspace;
+  a.sk_part = (float*)((char*)workspace + pkv::kWsHeaderBytes);
+  a.seq_begin = prefix_lens;
+  a.pre_part = pre_part;
+  a.pre_splits = plan.splits;
+  hipError_t e = pkv::launch_decode_streamk(a, stream);
   if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }

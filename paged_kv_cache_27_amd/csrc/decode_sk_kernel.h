@@ -120,15 +120,22 @@ struct Seg {
   int g, s, n;
 };
 
-template <int KV, int Q, int D, int GP, int NW, bool NT>
+// PRE: each sequence's first seq_begin[s] tokens were attended by the shared-prefix
+// kernel, which left pre_splits partials per (sequence, query head) in pre_part; this
+// kernel streams only the rest of each context and folds those partials in wherever it
+// writes a final output.  A piece covering a whole segment then waits in a third LDS
+// slot of its wave for that fold instead of being written straight out.
+template <int KV, int Q, int D, int GP, int NW, bool NT, bool PRE>
 __global__ void __launch_bounds__(64 * NW)
 decode_sk_kernel(const DecodeArgs a) {
   using W = Decoder<KV, Q, D, GP, NT>;
   using L_ = SkLayout<GP, D>;
   using RS = RowSet<GP, D>;
+  constexpr int NSLOT = PRE ? 3 : 2;
+  constexpr int PSTRIDE = 4 + D;  // floats per prefix partial: m, l, pad, pad, acc[D]
 
   extern __shared__ int sk_cum[];  // [N + 1]: chunks of sequences before s
-  __shared__ __attribute__((aligned(16))) float lds_part[2 * NW][L_::STRIDE];  // 2 per wave
+  __shared__ __attribute__((aligned(16))) float lds_part[NSLOT * NW][L_::STRIDE];
   __shared__ int lds_count[NW];    // arrivals at the segment whose first wave is i
   __shared__ float lds_p[NW][16 * GP];
   __shared__ float lds_alpha[NW][GP];
@@ -142,8 +149,13 @@ decode_sk_kernel(const DecodeArgs a) {
   // ---- exclusive prefix of per-sequence chunk counts, in LDS ----
   const int per = (N + NTH - 1) / NTH;
   const int i0s = min(N, tid * per), i1s = min(N, i0s + per);
+  // chunks of sequence i this kernel streams (after its shared prefix when PRE)
+  auto chunks_of = [&](int i) {
+    const int n = (a.context_lens[i] + 15) >> 4;
+    return PRE ? max(0, n - (a.seq_begin[i] >> 4)) : n;
+  };
   int local = 0;
-  for (int i = i0s; i < i1s; ++i) local += (a.context_lens[i] + 15) >> 4;
+  for (int i = i0s; i < i1s; ++i) local += chunks_of(i);
   int incl = local;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -157,7 +169,7 @@ decode_sk_kernel(const DecodeArgs a) {
   for (int w2 = 0; w2 < wv; ++w2) run_sum += wave_tot[w2];
   for (int i = i0s; i < i1s; ++i) {
     sk_cum[i] = run_sum;
-    run_sum += (a.context_lens[i] + 15) >> 4;
+    run_sum += chunks_of(i);
   }
   if (tid == NTH - 1) sk_cum[N] = run_sum;
   __syncthreads();
@@ -167,13 +179,38 @@ decode_sk_kernel(const DecodeArgs a) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const float vnorm = KV == kFP8 ? a.v_scale : 1.0f;
 
-  // Empty contexts own no unit: their outputs are zeros, spread over all waves.
+  // Fold the prefix partials of (sequence s, KV head g) into rs (PRE, s has a prefix).
+  auto add_prefix = [&](RS& rs, int s, int g) {
+    if constexpr (PRE) {
+      if (a.seq_begin[s] <= 0) return;
+      for (int t = 0; t < a.pre_splits; ++t) {
+#pragma unroll
+        for (int k = 0; k < RS::EPL; ++k) {
+          const float* pp = a.pre_part +
+              (((size_t)s * a.num_q_heads + (size_t)g * G + rs.hh[k]) * a.pre_splits + t) * PSTRIDE;
+          rs.add(k, pp[0], pp[1], *(const float4*)(pp + 4 + rs.dd[k]));
+        }
+      }
+    }
+  };
+
+  // Contexts with no chunk to stream own no unit: zeros, or (PRE) their prefix alone;
+  // spread over all waves.
   {
     const long long Wl = (long long)gridDim.x * NW, w = (long long)blockIdx.x * NW + wv;
     for (long long s = w; s < N; s += Wl) {
       if (sk_cum[s + 1] != sk_cum[s]) continue;
       const size_t row0 = (size_t)s * a.num_q_heads * D;
-      for (int i = lane; i < a.num_q_heads * D; i += 64) store_out(a.out, row0 + i, a.out_dtype, 0.0f);
+      if (PRE && a.seq_begin[s] > 0) {
+        for (int g = 0; g < a.num_kv_heads; ++g) {
+          RS rs;
+          rs.init(lane, G);
+          add_prefix(rs, (int)s, g);
+          rs.write_out(a, row0 + (size_t)g * G * D, vnorm);
+        }
+      } else {
+        for (int i = lane; i < a.num_q_heads * D; i += 64) store_out(a.out, row0 + i, a.out_dtype, 0.0f);
+      }
     }
   }
 
@@ -215,8 +252,9 @@ decode_sk_kernel(const DecodeArgs a) {
   // Units [u0, u1) of segment X.
   auto do_piece = [&](const Seg& X, long long u0, long long u1) {
     const int cb = (int)(u0 - X.xs), ce = (int)(u1 - X.xs);
+    const int cb0 = PRE ? (a.seq_begin[X.s] >> 4) : 0;  // first streamed chunk of the context
     wd.begin(a, X.s, X.g, a.context_lens[X.s]);
-    run_chunks(wd, cb, ce, 1);
+    run_chunks(wd, cb0 + cb, cb0 + ce, 1);
     wd.finish();
     float Mh[GP], Lh[GP];
 #pragma unroll
@@ -225,7 +263,8 @@ decode_sk_kernel(const DecodeArgs a) {
       Lh[h] = wd.head_l(h);
     }
     const size_t row0 = ((size_t)X.s * a.num_q_heads + (size_t)X.g * G) * D;
-    if (cb == 0 && ce == X.n) {  // the whole context: final output
+    const bool full = cb == 0 && ce == X.n;
+    if (!PRE && full) {  // the whole context: final output
       if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < GP; ++h) lds_inv[wv][h] = Lh[h] != 0.0f ? vnorm / Lh[h] : 0.0f;
@@ -237,9 +276,10 @@ decode_sk_kernel(const DecodeArgs a) {
       wave_lds_sync();
       return;
     }
-    // Partial: slot 1 if the piece starts the segment (then it continues past this
-    // wave), slot 0 if it continues one that started before this wave's range.
-    float* lp = lds_part[2 * wv + (cb == 0 ? 1 : 0)];
+    // Partial: slot 1 if the piece starts the segment and continues past this wave,
+    // slot 0 if it continues one that started before this wave's range, slot 2 (PRE)
+    // if it is the whole segment.
+    float* lp = lds_part[NSLOT * wv + (full ? 2 : (cb == 0 ? 1 : 0))];
     wd.visit([&](int h, int d, float v) { lp[L_::ACC + h * D + d] = v; });
     if (lane == 0) {
 #pragma unroll
@@ -251,6 +291,18 @@ decode_sk_kernel(const DecodeArgs a) {
     // The waves of this workgroup that cover X: i0 .. i1.
     const int i0 = (int)split_owner(Lb, NWn, max(X.xs, ub) - ub);
     const int i1 = (int)split_owner(Lb, NWn, min(X.xe, ue) - 1 - ub);
+    if (PRE && full) {  // this wave holds the whole segment: fold in the prefix, write
+      wave_lds_sync();
+      RS rs;
+      rs.init(lane, G);
+#pragma unroll
+      for (int k = 0; k < RS::EPL; ++k)
+        rs.add(k, lp[rs.hh[k]], lp[GP + rs.hh[k]], *(const float4*)(lp + L_::ACC + rs.hh[k] * D + rs.dd[k]));
+      add_prefix(rs, X.s, X.g);
+      rs.write_out(a, row0, vnorm);
+      wave_lds_sync();  // the slot is reused by this wave's next whole segment
+      return;
+    }
     if (i1 > i0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       int prev = 0;
@@ -269,12 +321,13 @@ decode_sk_kernel(const DecodeArgs a) {
     rs.init(lane, G);
     for (int i = i0; i <= i1; ++i) {
       const int sl = (i == i0 && X.xs >= ub + split_begin(Lb, NWn, i0)) ? 1 : 0;
-      const float* q = lds_part[2 * i + sl];
+      const float* q = lds_part[NSLOT * i + sl];
 #pragma unroll
       for (int k = 0; k < RS::EPL; ++k)
         rs.add(k, q[rs.hh[k]], q[GP + rs.hh[k]], *(const float4*)(q + L_::ACC + rs.hh[k] * D + rs.dd[k]));
     }
     if (X.xs >= ub && X.xe <= ue) {  // X lies inside this workgroup's range
+      add_prefix(rs, X.s, X.g);
       rs.write_out(a, row0, vnorm);
       return;
     }
@@ -317,6 +370,7 @@ decode_sk_kernel(const DecodeArgs a) {
         fin.add(k, m, l, make_float4(bits_f32(x.x), bits_f32(x.y), bits_f32(x.z), bits_f32(x.w)));
       }
     }
+    add_prefix(fin, X.s, X.g);
     fin.write_out(a, row0, vnorm);
     if (lane == 0) __hip_atomic_store(a.sk_count + b0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
@@ -350,7 +404,7 @@ decode_sk_kernel(const DecodeArgs a) {
 
 // Launcher of one instantiation; explicitly instantiated per cache dtype in
 // decode_sk_<dtype>.hip.
-template <int KV, int Q, int D, int GP, bool NT>
+template <int KV, int Q, int D, int GP, bool NT, bool PRE = false>
 struct SkKernels {
   static constexpr int NW = SkShape<KV, GP>::NW;
   static constexpr int STRIDE = SkLayout<GP, D>::STRIDE;
@@ -359,15 +413,15 @@ struct SkKernels {
 };
 
 #ifdef PKV_SK_DEFINE
-template <int KV, int Q, int D, int GP, bool NT>
-const void* SkKernels<KV, Q, D, GP, NT>::decode() {
-  return (const void*)&decode_sk_kernel<KV, Q, D, GP, NW, NT>;
+template <int KV, int Q, int D, int GP, bool NT, bool PRE>
+const void* SkKernels<KV, Q, D, GP, NT, PRE>::decode() {
+  return (const void*)&decode_sk_kernel<KV, Q, D, GP, NW, NT, PRE>;
 }
-template <int KV, int Q, int D, int GP, bool NT>
-hipError_t SkKernels<KV, Q, D, GP, NT>::launch(const DecodeArgs& a, hipStream_t stream) {
+template <int KV, int Q, int D, int GP, bool NT, bool PRE>
+hipError_t SkKernels<KV, Q, D, GP, NT, PRE>::launch(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
-  hipLaunchKernelGGL((decode_sk_kernel<KV, Q, D, GP, NW, NT>), dim3(a.sk_workers / NW), dim3(64 * NW), lds,
-                     stream, a);
+  hipLaunchKernelGGL((decode_sk_kernel<KV, Q, D, GP, NW, NT, PRE>), dim3(a.sk_workers / NW), dim3(64 * NW),
+                     lds, stream, a);
   return hipGetLastError();
 }
 #endif
@@ -382,5 +436,8 @@ hipError_t SkKernels<KV, Q, D, GP, NT>::launch(const DecodeArgs& a, hipStream_t 
 #define PKV_SK_EXTERN(KV, Q, D, GP)                      \
   extern template struct SkKernels<KV, Q, D, GP, true>;  \
   extern template struct SkKernels<KV, Q, D, GP, false>;
+// the suffix pass of the shared-prefix decode: private blocks, streaming loads
+#define PKV_SK_INSTANTIATE_PRE(KV, Q, D, GP) template struct SkKernels<KV, Q, D, GP, true, true>;
+#define PKV_SK_EXTERN_PRE(KV, Q, D, GP) extern template struct SkKernels<KV, Q, D, GP, true, true>;
 
 }  // namespace pkv

@@ -45,7 +45,30 @@ struct DecodeArgs {
   int32_t sk_workers;      // waves in the launch
   int32_t* sk_count;       // [workgroups] arrival counters: zero on entry, zero on exit
   float* sk_part;          // [2 * workgroups] partials: m[GP], l[GP], (16-byte aligned) acc[GP][D]
+  // suffix pass of the shared-prefix decode (balanced schedule only; null otherwise)
+  const int32_t* seq_begin;  // [N] tokens of each context already attended (a multiple of 16)
+  const float* pre_part;     // [N][H_q][pre_splits][4 + D]: m, l, pad, pad, acc
+  int32_t pre_splits;
 };
+
+// Shared-prefix (cascade) pass: partials of every group's shared prefix.
+struct PrefixArgs {
+  const void* q;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
+  int cache_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* group_starts;  // [groups + 1]
+  const int32_t* prefix_lens;   // [N]
+  float scale;
+  float* pre_part;              // [N][H_q][splits][4 + D]
+  int32_t splits;               // slices of each prefix's chunks
+  int32_t tiles;                // 128-row tiles per group
+};
+constexpr int kPrefixRows = 128;  // query rows per workgroup of the prefix kernel
+hipError_t launch_prefix(const PrefixArgs& a, int num_groups, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t n,
                                const int32_t* block_tables, int32_t max_blocks,
@@ -68,7 +91,7 @@ struct SkPlan {
 };
 int pad_group(int G);
 int streamk_plan(int cache_dtype, int q_dtype, int head_dim, int group, int num_seqs, bool kv_stream,
-                 SkPlan* out);
+                 bool pre, SkPlan* out);
 
 // Every workspace starts with a header of arrival counters (one int per workgroup of
 // a balanced launch) that is zero before the first call and that every call leaves

@@ -1,0 +1,292 @@
+// Shared-prefix decode for gfx950: the prefix half of cascade attention.
+//
+// With prefix caching several sequences map their first blocks to the same physical
+// blocks ("La despensa por casilleros", section "Prefix caching: compartir casilleros
+// con copy-on-write"; "PagedAttention por dentro...", section "Compartir prefijos").
+// Attention over those shared tokens is the same matrix product for every sequence of
+// the group, so it is computed once for all of them: the queries of the group's
+// sequences (for one KV head: n_seqs x G rows) are the rows of
+//   S = Q K^T,  P = online-softmax(S),  O = P V
+// over the prefix tokens, and each row leaves a partial result (running max m in the
+// log2 domain, denominator l, unnormalised output acc) that the suffix pass merges
+// with the sequence's own tokens by the log-sum-exp algebra of the online softmax
+// ("Optimizacion de Inferencia LLM", sections "PagedAttention: Conceptos de SO..."
+// and "FlashAttention-3...").
+//
+// One workgroup = 8 waves x 16 query rows of one (group, KV head), over one slice of
+// the prefix's 16-token chunks (the slices are merged later with the suffix).  Per
+// chunk and wave, on the matrix cores:
+//   * S^T = K Q^T: 16x16x32 MFMAs, A = the K tile rows as loaded (lane l: token l%16,
+//     8 dims), B = the wave's 16 query rows; lane l gets row l%16 against tokens
+//     4(l/16) .. 4(l/16)+3;
+//   * that is exactly the A operand of the 16x16x16 P.V MFMA (row l%16, k = tokens
+//     4(l/16)+i), so P never leaves registers (split hi + lo in 16 bits, ~16 bits of
+//     each probability kept);
+//   * V's B operand needs 4 consecutive tokens of one dim per lane: the workgroup
+//     stages each V tile once in LDS as [4-token group][dim][4 tokens], so a lane's
+//     fragment is one conflict-free 8-byte LDS read.
+// K tiles are staged in LDS the same way (row stride padded by 16 bytes, so a wave's
+// 16-byte A-fragment reads hit distinct banks); the loads of the next chunks are in
+// flight in registers while one is computed.  Workgroups of one KV head are placed on
+// one XCD (workgroup i runs on XCD i mod 8) so the head's shared tiles stay in that L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+template <int KV> struct PfxOps;
+template <> struct PfxOps<kBF16> {
+  using frag8 = bf16x8_t;
+  typedef __bf16 frag4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+  __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4_t pv(frag4 a, frag4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // p = hi + lo: hi the upper half of p's fp32 bits, lo the bf16 truncation of the rest
+  __device__ __forceinline__ static uint32_t hi16(float p) { return f32_bits(p) >> 16; }
+  __device__ __forceinline__ static uint32_t lo16(float p) {
+    return f32_bits(p - bits_f32(f32_bits(p) & 0xffff0000u)) >> 16;
+  }
+};
+template <> struct PfxOps<kF16> {
+  using frag8 = f16x8_t;
+  typedef _Float16 frag4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
+  __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4_t pv(frag4 a, frag4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t hi16(float p) {
+    return __builtin_bit_cast(uint16_t, (_Float16)p);
+  }
+  __device__ __forceinline__ static uint32_t lo16(float p) {
+    const _Float16 h = (_Float16)p;
+    return __builtin_bit_cast(uint16_t, (_Float16)(p - (float)h));
+  }
+};
+
+__device__ __forceinline__ float pf_xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
+  return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+}
+__device__ __forceinline__ float pf_xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+  return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+}
+__device__ __forceinline__ float pf_xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
+  return bits_f32(r[0]) + bits_f32(r[1]);
+}
+__device__ __forceinline__ float pf_xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+  return bits_f32(r[0]) + bits_f32(r[1]);
+}
+
+constexpr int kPfxWaves = kPrefixRows / 16;
+constexpr int kPfxRows = kPrefixRows;
+#ifndef PKV_PFX_DEPTH
+#define PKV_PFX_DEPTH 6
+#endif
+constexpr int PD = PKV_PFX_DEPTH;  // chunks whose loads are in flight
+
+template <int KV, int D>
+__global__ void __launch_bounds__(64 * kPfxWaves) prefix_kernel(const PrefixArgs a) {
+  using O_ = PfxOps<KV>;
+  constexpr int ROW = 2 * D;          // bytes of one K/V row
+  constexpr int NKC = D / 32;         // 16x16x32 MFMAs per chunk (K dims)
+  constexpr int NJ = D / 16;          // 16-dim output tiles
+  constexpr int KSTAGE = 16 * (D / 8); // threads staging K: 16 rows x D/8 16-byte pieces
+  constexpr int VSTAGE = 4 * (D / 2);  // threads staging V: 4 token groups x D/2 dim pairs
+  constexpr int KROW = D + 8;          // K row stride in LDS (elements): conflict-free A reads
+  constexpr int STRIDE = 4 + D;        // floats per partial: m, l, pad, pad, acc[D]
+  static_assert(KSTAGE <= 256 && VSTAGE <= 256, "K staged by threads 0..255, V by 256..511");
+  // K tile as [token][KROW], V tile as [token group tg][dim d][token 4tg + e], 16-bit.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][16 * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][4 * D * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int Hkv = a.num_kv_heads, G = a.num_q_heads / Hkv, T = a.splits;
+  int bid = blockIdx.x;
+  const int g = bid % Hkv;
+  bid /= Hkv;
+  const int t = bid % T;
+  bid /= T;
+  const int tile = bid % a.tiles;
+  const int j = bid / a.tiles;
+  const int s0 = a.group_starts[j], s1 = a.group_starts[j + 1];
+  const int nrows = (s1 - s0) * G;
+  const int row0 = tile * kPfxRows;
+  if (row0 >= nrows) return;          // whole workgroup: no barrier reached
+  const int P = a.prefix_lens[s0];
+  if (P <= 0) return;                 // nothing shared: the suffix pass reads no partial
+  const int nch = P / 16;
+  const int c0 = nch * t / T, c1 = nch * (t + 1) / T;
+  const int32_t* bt = a.block_tables + (size_t)s0 * a.max_blocks_per_seq;
+  const int BS = a.block_size;
+  const uint8_t* kc = (const uint8_t*)a.k_cache;
+  const uint8_t* vc = (const uint8_t*)a.v_cache;
+  const float scale_l2 = a.scale * kLog2e;
+
+  // ---- this lane's query row (B operand of S^T = K Q^T: row l%16, dims 8(l/16) + 32c)
+  const int rq = row0 + 16 * wv + (lane & 15);
+  const bool qvalid = rq < nrows;
+  const uint8_t* qrow = (const uint8_t*)a.q +
+      ((size_t)(s0 + (qvalid ? rq / G : 0)) * a.num_q_heads + g * G + (qvalid ? rq % G : 0)) * ROW;
+  typename O_::frag8 qf[NKC];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c)
+    qf[c] = qvalid ? __builtin_bit_cast(typename O_::frag8, *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4))))
+                   : __builtin_bit_cast(typename O_::frag8, make_uint4(0, 0, 0, 0));
+
+  float m = kNegInf, l = 0.0f;
+  f32x4_t O[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) O[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto tile_off = [&](int c) {  // byte offset of chunk c's (block, KV head) rows
+    const int tok = 16 * c;
+    const int blk = bt[tok / BS];
+    return (((size_t)blk * Hkv + g) * BS + (tok % BS)) * ROW;
+  };
+  // Staging threads: 0..KSTAGE-1 copy one 16-byte piece of the K tile (row kr, piece kp);
+  // 256..256+VSTAGE-1 one dim pair of 4 V tokens (tokens 4tg .. 4tg+3, dims 2dp, 2dp+1).
+  // Every thread issues both loads, the ones it has no part in through an empty resource.
+  const int kr = (tid / (D / 8)) & 15, kp = tid % (D / 8);
+  const int vt = tid - 256;
+  const int tg = (vt / (D / 2)) & 3, dp = (vt & 0xffff) % (D / 2);
+  const bool kstage = tid < KSTAGE, vstage = vt >= 0 && vt < VSTAGE;
+  struct Stage {
+    uint4 k;
+    uint32_t v[4];
+  };
+  // live == false: padding past the slice, reads nothing.
+  auto issue = [&](int c, bool live, Stage& st) {
+    const size_t off = tile_off(min(c, c1 - 1));
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc + off, live && kstage ? 16 * ROW : 0);
+    const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vc + off, live && vstage ? 16 * ROW : 0);
+    st.k = load_kv16<false>(krs, kr * ROW + 16 * kp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.v[e] = load_kv4<false>(vrs, (4 * tg + e) * ROW + 4 * dp);
+  };
+  auto stage = [&](int buf, const Stage& st) {
+    if (kstage) *(uint4*)&lds_k[buf][kr * KROW + 8 * kp] = st.k;
+    if (vstage) {
+      // dim 2dp: the low halves of the 4 tokens' words, dim 2dp+1: the high halves
+      const uint32_t lo01 = __builtin_amdgcn_perm(st.v[1], st.v[0], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(st.v[3], st.v[2], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(st.v[1], st.v[0], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(st.v[3], st.v[2], 0x07060302u);
+      uint16_t* base = &lds_v[buf][(tg * D + 2 * dp) * 4];
+      *(uint2*)base = make_uint2(lo01, lo23);
+      *(uint2*)(base + 4) = make_uint2(hi01, hi23);
+    }
+  };
+  // One chunk from LDS buffer buf: S^T = K Q^T, online softmax, O += P V.
+  auto compute = [&](int buf) {
+    // A = K rows: lane l reads token l%16, dims 32cc + 8(l/16); S^T lane l: row l%16
+    // against tokens 4(l/16) + i
+    f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cc = 0; cc < NKC; ++cc) {
+      const uint4 kf = *(const uint4*)&lds_k[buf][(lane & 15) * KROW + 32 * cc + 8 * (lane >> 4)];
+      S = O_::qk(__builtin_bit_cast(typename O_::frag8, kf), qf[cc], S);
+    }
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = S[i] * scale_l2;
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bm = pf_xor32_max(pf_xor16_max(bm));
+    const float mn = fmaxf(m, bm);  // finite: every prefix token is a real token
+    const float alpha = fast_exp2(m - mn);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - mn);
+    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    const bool changed = mn > m;
+    m = mn;
+    if (__ballot(changed) != 0) {
+      // O rows 4(l/16) + i take the factor of row 4(l/16) + i, held by lane 4(l/16) + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * (lane >> 4) + i);
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) O[jj][i] *= ai;
+      }
+    }
+    const uint32_t h0 = O_::hi16(p[0]) | (O_::hi16(p[1]) << 16), h1 = O_::hi16(p[2]) | (O_::hi16(p[3]) << 16);
+    const uint32_t l0 = O_::lo16(p[0]) | (O_::lo16(p[1]) << 16), l1 = O_::lo16(p[2]) | (O_::lo16(p[3]) << 16);
+    const auto ahi = __builtin_bit_cast(typename O_::frag4, make_uint2(h0, h1));
+    const auto alo = __builtin_bit_cast(typename O_::frag4, make_uint2(l0, l1));
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const uint2 vv = *(const uint2*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 4];
+      const auto vf = __builtin_bit_cast(typename O_::frag4, vv);
+      O[jj] = O_::pv(ahi, vf, O[jj]);
+      O[jj] = O_::pv(alo, vf, O[jj]);
+    }
+  };
+
+  // Chunks c0 .. c1-1 with the loads of the next PD chunks in flight (a register ring,
+  // rotated by a fully unrolled inner loop; every step issues its loads unconditionally,
+  // padding ones through an empty resource), staged in LDS one chunk ahead.
+  if (c0 < c1) {
+    const int n = c1 - c0;
+    Stage ring[PD];
+#pragma unroll
+    for (int u = 0; u < PD; ++u) issue(c0 + u, u < n, ring[u]);
+    stage(0, ring[0]);
+    __syncthreads();
+    for (int i = 0; i < n; i += PD) {
+#pragma unroll
+      for (int u = 0; u < PD; ++u) {
+        const int ii = i + u;
+        if (ii >= n) break;
+        compute(ii & 1);
+        if (ii + 1 < n) stage((ii + 1) & 1, ring[(u + 1) % PD]);
+        issue(c0 + ii + PD, ii + PD < n, ring[u]);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- partials: m, l per row (lanes 0..15), acc rows 4(l/16) + i, dims 16jj + l%16
+  const float lsum = pf_xor32_sum(pf_xor16_sum(l));
+  auto part_of = [&](int rr) {
+    return a.pre_part + (((size_t)(s0 + rr / G) * a.num_q_heads + g * G + rr % G) * T + t) * STRIDE;
+  };
+  if (lane < 16 && qvalid) {
+    float* pp = part_of(rq);
+    pp[0] = m;
+    pp[1] = lsum;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
+    if (rr >= nrows) continue;
+    float* pp = part_of(rr) + 4;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) pp[16 * jj + (lane & 15)] = O[jj][i];
+  }
+}
+
+// ---- dispatch --------------------------------------------------------------------
+hipError_t launch_prefix(const PrefixArgs& a, int num_groups, hipStream_t stream) {
+  const dim3 grid((unsigned)num_groups * a.tiles * a.splits * a.num_kv_heads);
+  const dim3 block(64 * kPfxWaves);
+#define PKV_PFX(KV, D) hipLaunchKernelGGL((prefix_kernel<KV, D>), grid, block, 0, stream, a)
+  if (a.cache_dtype == kBF16 && a.head_dim == 128) PKV_PFX(kBF16, 128);
+  else if (a.cache_dtype == kBF16 && a.head_dim == 64) PKV_PFX(kBF16, 64);
+  else if (a.cache_dtype == kF16 && a.head_dim == 128) PKV_PFX(kF16, 128);
+  else if (a.cache_dtype == kF16 && a.head_dim == 64) PKV_PFX(kF16, 64);
+  else return hipErrorInvalidValue;
+#undef PKV_PFX
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -26,6 +26,8 @@ SMALL = {
     "llama8b": LLAMA8B.replace(num_seqs=3, ctx_params=(17, 70)),
     "r70b": R70B_FP8.replace(num_seqs=3, ctx_params=(48, 0.5, 16, 100)),
     "prefix": PREFIX.replace(num_seqs=4, ctx_params=(64, 0, 40)),
+    "prefix-groups": PREFIX.replace(name="prefix-groups", num_seqs=7, prefix_groups=3,
+                                    ctx_params=(64, 0, 40)),
     "longctx": LONGCTX.replace(num_seqs=2, ctx_params=(200,)),
     "mha-f16": TINY.replace(name="mha-f16", num_q_heads=4, num_kv_heads=4, q_dtype="f16",
                             kv_dtype="f16", src_dtype="f16", out_dtype="f16", pool_blocks=0,

@@ -142,3 +142,29 @@ def test_even_split_owner_formula():
             for p in range(P):
                 for x in range(T * p // P, T * (p + 1) // P):
                     assert ((x + 1) * P - 1) // T == p, (T, P, x)
+
+
+def _prefix_call(lib, desc, q_dtype=pkv.BF16, n=4, hq=4, maxb=8, maxctx=100, groups=1, gmax=4,
+                 pmax=32, ws=FAKE, wsb=1 << 30, gs=FAKE, pl=FAKE):
+    return lib.paged_attention_decode_shared_prefix(
+        FAKE, q_dtype, n, hq, FAKE, FAKE, ctypes.byref(desc), FAKE, maxb, FAKE, maxctx, gs, groups,
+        gmax, pl, pmax, 0.1, FAKE, q_dtype, ws, wsb, None)
+
+
+def test_shared_prefix_argument_errors():
+    lib = pkv.load_library()
+    assert _prefix_call(lib, _desc(dtype=pkv.FP8_E4M3)) == -2  # 16-bit caches only
+    assert _prefix_call(lib, _desc(dtype=pkv.F32), q_dtype=pkv.F32) == -2
+    assert _prefix_call(lib, _desc(), pmax=24) == -3  # not a multiple of the block size
+    assert _prefix_call(lib, _desc(), pmax=112) == -3  # longer than the longest context
+    assert _prefix_call(lib, _desc(), groups=0) == -3
+    assert _prefix_call(lib, _desc(), groups=5) == -3  # more groups than sequences
+    assert _prefix_call(lib, _desc(), gs=None) == -1
+    assert _prefix_call(lib, _desc(), pl=None) == -1
+    assert _prefix_call(lib, _desc(), ws=None) == -1
+    need = pkv.paged_attention_shared_prefix_workspace_size(_desc(), pkv.BF16, 4, 4, 100, 1, 4, 32)
+    assert need > pkv.WORKSPACE_HEADER_BYTES
+    assert _prefix_call(lib, _desc(), wsb=need - 1) == -5
+    assert _prefix_call(lib, _desc(), n=0) == 0
+    assert pkv.paged_attention_shared_prefix_workspace_size(_desc(dtype=pkv.FP8_E4M3), pkv.BF16,
+                                                            4, 4, 100, 1, 4, 32) == 0

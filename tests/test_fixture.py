@@ -84,3 +84,27 @@ def test_tiny_shape():
     assert w.context_lens.tolist() == [7, 16, 33, 100]
     # 1 + 1 + 3 + 7 live blocks
     assert sum((int(c) + 15) // 16 for c in w.context_lens) == 12
+
+
+def test_prefix_groups_share_within_group_only():
+    """Several prefix groups: each group's sequences share that group's prefix blocks
+    (refcount = group size) and no block is shared across groups."""
+    cfg = PREFIX.replace(num_seqs=7, prefix_groups=3, ctx_params=(64, 0, 40))
+    w = make_workload(cfg)
+    starts = w.prefix_group_starts()
+    assert list(starts) == [0, 2, 4, 7]
+    shared_n = 64 // cfg.block_size
+    heads = []
+    for j in range(3):
+        a, b = starts[j], starts[j + 1]
+        head = w.block_tables[a, :shared_n]
+        for s in range(a, b):
+            assert (w.block_tables[s, :shared_n] == head).all()
+            assert w.prefix_owner(s) == a
+        assert (w.refcount[head] == b - a).all()
+        heads.append(set(head.tolist()))
+    assert not (heads[0] & heads[1]) and not (heads[1] & heads[2]) and not (heads[0] & heads[2])
+    # private blocks are private: every other live block has refcount 1
+    live = set(w.block_tables[w.block_tables != w.sentinel_block].tolist())
+    for blk in live - heads[0] - heads[1] - heads[2]:
+        assert w.refcount[blk] == 1

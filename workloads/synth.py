@@ -58,6 +58,9 @@ class DecodeConfig:
     pool_factor: float = 1.25
     pool_blocks: int = 0  # explicit pool size (0 = ceil(pool_factor * live) + 1)
     seed: int = 0
+    # "prefix" contexts: the sequences form this many contiguous groups (group k is
+    # sequences [N k / groups, N (k+1) / groups)); each group shares its own prefix blocks.
+    prefix_groups: int = 1
 
     @property
     def group(self) -> int:
@@ -186,6 +189,17 @@ class Workload:
     def new_pos(self) -> np.ndarray:
         return (self.context_lens - 1).astype(np.int32)
 
+    def prefix_group_starts(self) -> np.ndarray:
+        """First sequence of each prefix-sharing group, then num_seqs (int32)."""
+        n = self.cfg.num_seqs
+        k = self.cfg.prefix_groups if self.cfg.ctx_kind == "prefix" else 1
+        return np.array([n * i // k for i in range(k + 1)], dtype=np.int32)
+
+    def prefix_owner(self, s: int) -> int:
+        """The sequence whose cached rows hold s's shared prefix (its group's first)."""
+        starts = self.prefix_group_starts()
+        return int(starts[np.searchsorted(starts, s, side="right") - 1])
+
     def logical_kv(self, s: int):
         """K and V of sequence s in logical token order (src storage), new token last."""
         ctx = int(self.context_lens[s])
@@ -193,8 +207,9 @@ class Workload:
         prefix = self._shared_prefix_len()
         for row in np.nonzero(self.hist_seq == s)[0]:
             pos_to_row[int(self.hist_pos[row])] = int(row)
-        if prefix and s != 0:
-            for row in np.nonzero((self.hist_seq == 0) & (self.hist_pos < prefix))[0]:
+        owner = self.prefix_owner(s) if prefix else s
+        if prefix and s != owner:
+            for row in np.nonzero((self.hist_seq == owner) & (self.hist_pos < prefix))[0]:
                 pos_to_row[int(self.hist_pos[row])] = int(row)
         rows = [pos_to_row[p] for p in range(ctx - 1)]
         k = np.concatenate([self.hist_k[rows], self.new_k[s:s + 1]], axis=0)
@@ -215,7 +230,8 @@ class Workload:
         prefix = self._shared_prefix_len()
         tokens = int(self.context_lens.astype(np.int64).sum())
         if prefix:
-            tokens -= prefix * (c.num_seqs - 1)
+            groups = len(self.prefix_group_starts()) - 1
+            tokens -= prefix * (c.num_seqs - groups)
         return tokens * c.num_kv_heads * c.head_dim * 2 * DTYPE_BYTES[c.kv_dtype]
 
 
@@ -263,28 +279,35 @@ def make_workload(cfg: DecodeConfig, seed: int | None = None,
     prefix = int(cfg.ctx_params[0]) if cfg.ctx_kind == "prefix" else 0
     assert prefix % B == 0, "a shared prefix must end on a block boundary"
     shared_n = prefix // B
-    live = int(nblk.sum()) - shared_n * max(N - 1, 0)
+    ngroups = cfg.prefix_groups if prefix else 1
+    starts = [N * i // ngroups for i in range(ngroups + 1)]
+    first = set(starts[:-1])  # the first sequence of each group owns its prefix rows
+    live = int(nblk.sum()) - shared_n * max(N - ngroups, 0)
     num_blocks = cfg.pool_blocks or int(math.ceil(cfg.pool_factor * live)) + 1
     assert num_blocks >= live + 1, "pool too small for the live blocks plus the sentinel"
 
     pool = BlockPool(num_blocks, rng)
     max_blocks = max(int(nblk.max()) if N else 1, 1)
     tables = np.empty((N, max_blocks), dtype=np.int32)
-    shared = [pool.allocate() for _ in range(shared_n)]
+    shared = [pool.allocate() for _ in range(shared_n)]  # group 0's prefix blocks
+    all_shared = list(shared)
     for s in range(N):
+        if s in first and s > 0:  # a later group: its own prefix blocks
+            shared = [pool.allocate() for _ in range(shared_n)]
+            all_shared += shared
         ids = []
         for j in range(int(nblk[s])):
-            ids.append(pool.share(shared[j]) if j < shared_n and s > 0 else
+            ids.append(pool.share(shared[j]) if j < shared_n and s not in first else
                        (shared[j] if j < shared_n else pool.allocate()))
         tables[s, :len(ids)] = ids
         tables[s, len(ids):] = -2  # filled below with the sentinel
     sentinel = pool.allocate()
     tables[tables == -2] = sentinel
 
-    # Cached history: every position before the new token; the shared prefix once.
+    # Cached history: every position before the new token; each shared prefix once.
     seqs, poss = [], []
     for s in range(N):
-        start = prefix if (prefix and s > 0) else 0
+        start = prefix if (prefix and s not in first) else 0
         n_hist = int(ctx[s]) - 1 - start
         if n_hist > 0:
             seqs.append(np.full(n_hist, s, np.int32))
@@ -312,7 +335,7 @@ def make_workload(cfg: DecodeConfig, seed: int | None = None,
                     refcount=pool.refcount.copy(), free_blocks=pool.free_ids(),
                     hist_seq=hist_seq, hist_pos=hist_pos, hist_k=hist_k, hist_v=hist_v,
                     new_k=new_k, new_v=new_v, q=q, k_scale=k_scale, v_scale=v_scale,
-                    scale=float(np.float32(1.0 / math.sqrt(D))), shared_blocks=shared)
+                    scale=float(np.float32(1.0 / math.sqrt(D))), shared_blocks=all_shared)
 
 
 def cache_shape(w: Workload) -> tuple:
