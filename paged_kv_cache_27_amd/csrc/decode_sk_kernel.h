@@ -57,8 +57,6 @@ template <int KV, int GP> struct SkShape {
   static constexpr int NW = KV == kF32 ? 4 : (GP <= 8 ? 8 : 4);
 };
 
-constexpr int kAuxDevice = 16;  // buffer-access cache policy bit: device scope (sc1)
-
 // floor-division split of T items into P parts: part p holds [T p / P, T (p+1) / P);
 // owner(x) is the part holding item x (T >= P >= 1, so no part is empty).
 __device__ __forceinline__ long long split_begin(long long T, long long P, long long p) { return T * p / P; }
@@ -180,16 +178,33 @@ decode_sk_kernel(const DecodeArgs a) {
   const float vnorm = KV == kFP8 ? a.v_scale : 1.0f;
 
   // Fold the prefix partials of (sequence s, KV head g) into rs (PRE, s has a prefix).
+  // The slices' loads go out in batches (as many as 8 partial elements of registers
+  // allow) so a fold waits for memory once per batch, not once per slice; a batch's
+  // entries past the last slice re-read it and weigh nothing (m = -inf).
   auto add_prefix = [&](RS& rs, int s, int g) {
     if constexpr (PRE) {
       if (a.seq_begin[s] <= 0) return;
-      for (int t = 0; t < a.pre_splits; ++t) {
+      constexpr int BATCH = RS::EPL >= 8 ? 1 : 8 / RS::EPL;
+      const int T = a.pre_splits;
+      const float* base = a.pre_part + ((size_t)s * a.num_q_heads + (size_t)g * G) * T * PSTRIDE;
+      for (int t0 = 0; t0 < T; t0 += BATCH) {
+        float pm[BATCH][RS::EPL], pl[BATCH][RS::EPL];
+        float4 px[BATCH][RS::EPL];
 #pragma unroll
-        for (int k = 0; k < RS::EPL; ++k) {
-          const float* pp = a.pre_part +
-              (((size_t)s * a.num_q_heads + (size_t)g * G + rs.hh[k]) * a.pre_splits + t) * PSTRIDE;
-          rs.add(k, pp[0], pp[1], *(const float4*)(pp + 4 + rs.dd[k]));
+        for (int b = 0; b < BATCH; ++b) {
+          const int t = min(t0 + b, T - 1);
+#pragma unroll
+          for (int k = 0; k < RS::EPL; ++k) {
+            const float* pp = base + ((size_t)rs.hh[k] * T + t) * PSTRIDE;
+            pm[b][k] = t0 + b < T ? pp[0] : kNegInf;
+            pl[b][k] = pp[1];
+            px[b][k] = *(const float4*)(pp + 4 + rs.dd[k]);
+          }
         }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+          for (int k = 0; k < RS::EPL; ++k) rs.add(k, pm[b][k], pl[b][k], px[b][k]);
       }
     }
   };

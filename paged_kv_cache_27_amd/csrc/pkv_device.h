@@ -151,11 +151,20 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // gfx950, while for shared blocks it evicts lines other readers are about to reuse.
 constexpr int kRsrcWord3 = 0x00020000;  // raw untyped 32-bit buffer access on gfx9
 constexpr int kAuxNT = 2;               // buffer-load cache policy bit: nontemporal
+constexpr int kAuxDevice = 16;          // buffer-access cache policy bit: device scope (sc1)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// base and bytes must be the same in every lane of the wave.  They are moved to scalar
+// registers explicitly: a resource the compiler cannot prove uniform is wrapped, per
+// load, in a loop over the distinct values of the lanes, which also defeats its
+// vector-memory wait counting across a pipelined loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kRsrcWord3);
+  const uint64_t v = (uint64_t)(uintptr_t)base;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)u, (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 template <bool NT>
 __device__ __forceinline__ uint4 load_kv16(__amdgpu_buffer_rsrc_t r, int off) {

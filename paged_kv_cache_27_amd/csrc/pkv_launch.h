@@ -63,11 +63,11 @@ struct PrefixArgs {
   const int32_t* group_starts;  // [groups + 1]
   const int32_t* prefix_lens;   // [N]
   float scale;
-  float* pre_part;              // [N][H_q][splits][4 + D]
+  float* pre_part;              // [N][H_q][splits][4 + D]: m, l, pad, pad, acc
   int32_t splits;               // slices of each prefix's chunks
-  int32_t tiles;                // 128-row tiles per group
+  int32_t tiles;                // kPrefixRows-row tiles per group
 };
-constexpr int kPrefixRows = 128;  // query rows per workgroup of the prefix kernel
+constexpr int kPrefixRows = 64;  // query rows per workgroup of the prefix kernel
 hipError_t launch_prefix(const PrefixArgs& a, int num_groups, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t n,

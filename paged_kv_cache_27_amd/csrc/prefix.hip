@@ -91,21 +91,31 @@ __device__ __forceinline__ float pf_xor32_sum(float x) {
 constexpr int kPfxWaves = kPrefixRows / 16;
 constexpr int kPfxRows = kPrefixRows;
 #ifndef PKV_PFX_DEPTH
-#define PKV_PFX_DEPTH 6
+#define PKV_PFX_DEPTH 3
 #endif
 constexpr int PD = PKV_PFX_DEPTH;  // chunks whose loads are in flight
+constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay <= 2^8 between rescales
+// Four workgroups of four waves per CU (four waves per SIMD, <= 128 VGPRs each): a
+// workgroup waits at its per-chunk barrier while the others compute.
+constexpr int kPfxWavesPerSimd = 4;
 
 template <int KV, int D>
-__global__ void __launch_bounds__(64 * kPfxWaves) prefix_kernel(const PrefixArgs a) {
+__global__ void __launch_bounds__(64 * kPfxWaves) __attribute__((amdgpu_waves_per_eu(kPfxWavesPerSimd)))
+prefix_kernel(const PrefixArgs a) {
   using O_ = PfxOps<KV>;
   constexpr int ROW = 2 * D;          // bytes of one K/V row
   constexpr int NKC = D / 32;         // 16x16x32 MFMAs per chunk (K dims)
   constexpr int NJ = D / 16;          // 16-dim output tiles
+  constexpr int NT = 64 * kPfxWaves;   // threads of the workgroup
   constexpr int KSTAGE = 16 * (D / 8); // threads staging K: 16 rows x D/8 16-byte pieces
   constexpr int VSTAGE = 4 * (D / 2);  // threads staging V: 4 token groups x D/2 dim pairs
+  // V is staged by threads VOFF .. VOFF + VSTAGE - 1: the threads after the K stagers
+  // when both fit in the workgroup, else the same threads (each then stages both)
+  constexpr int VOFF = KSTAGE + VSTAGE <= NT ? KSTAGE : 0;
   constexpr int KROW = D + 8;          // K row stride in LDS (elements): conflict-free A reads
   constexpr int STRIDE = 4 + D;        // floats per partial: m, l, pad, pad, acc[D]
-  static_assert(KSTAGE <= 256 && VSTAGE <= 256, "K staged by threads 0..255, V by 256..511");
+  static_assert(KSTAGE <= NT && VOFF + VSTAGE <= NT && KSTAGE % 64 == 0 && VOFF % 64 == 0,
+                "K and V staged by whole waves of the workgroup");
   // K tile as [token][KROW], V tile as [token group tg][dim d][token 4tg + e], 16-bit.
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][16 * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][4 * D * 4];
@@ -155,10 +165,10 @@ __global__ void __launch_bounds__(64 * kPfxWaves) prefix_kernel(const PrefixArgs
     return (((size_t)blk * Hkv + g) * BS + (tok % BS)) * ROW;
   };
   // Staging threads: 0..KSTAGE-1 copy one 16-byte piece of the K tile (row kr, piece kp);
-  // 256..256+VSTAGE-1 one dim pair of 4 V tokens (tokens 4tg .. 4tg+3, dims 2dp, 2dp+1).
+  // VOFF..VOFF+VSTAGE-1 one dim pair of 4 V tokens (tokens 4tg .. 4tg+3, dims 2dp, 2dp+1).
   // Every thread issues both loads, the ones it has no part in through an empty resource.
   const int kr = (tid / (D / 8)) & 15, kp = tid % (D / 8);
-  const int vt = tid - 256;
+  const int vt = tid - VOFF;
   const int tg = (vt / (D / 2)) & 3, dp = (vt & 0xffff) % (D / 2);
   const bool kstage = tid < KSTAGE, vstage = vt >= 0 && vt < VSTAGE;
   struct Stage {
@@ -201,16 +211,17 @@ __global__ void __launch_bounds__(64 * kPfxWaves) prefix_kernel(const PrefixArgs
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = S[i] * scale_l2;
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = pf_xor32_max(pf_xor16_max(bm));
-    const float mn = fmaxf(m, bm);  // finite: every prefix token is a real token
-    const float alpha = fast_exp2(m - mn);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - mn);
-    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    const bool changed = mn > m;
-    m = mn;
-    if (__ballot(changed) != 0) {
+    bm = pf_xor32_max(pf_xor16_max(bm));  // finite: every prefix token is a real token
+    // Lazy rescaling: the reference max m moves only when a score exceeds it by more than
+    // kRescaleSlack (and on the first chunk, m = -inf), so weights 2^(s - m) stay <= 2^8.
+    // (m, l, acc) stay one consistent partial -- l and acc are sums of 2^(s - m) for the
+    // same m -- so the log-sum-exp merge is unchanged; only the rare rescale remains.
+    const bool move = bm > m + kRescaleSlack;
+    if (__ballot(move) != 0) {
+      const float mn = move ? bm : m;
+      const float alpha = fast_exp2(m - mn);  // 0 on the first chunk, 1 for rows kept
+      l *= alpha;
+      m = mn;
       // O rows 4(l/16) + i take the factor of row 4(l/16) + i, held by lane 4(l/16) + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -219,6 +230,10 @@ __global__ void __launch_bounds__(64 * kPfxWaves) prefix_kernel(const PrefixArgs
         for (int jj = 0; jj < NJ; ++jj) O[jj][i] *= ai;
       }
     }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
     const uint32_t h0 = O_::hi16(p[0]) | (O_::hi16(p[1]) << 16), h1 = O_::hi16(p[2]) | (O_::hi16(p[3]) << 16);
     const uint32_t l0 = O_::lo16(p[0]) | (O_::lo16(p[1]) << 16), l1 = O_::lo16(p[2]) | (O_::lo16(p[3]) << 16);
     const auto ahi = __builtin_bit_cast(typename O_::frag4, make_uint2(h0, h1));
