@@ -12,6 +12,8 @@
  *   oracle_decode        -- each query head's attention over its sequence's whole
  *                           cached context, read through the block table, with an
  *                           exact two-pass softmax in fp64.
+ *   oracle_decode_window -- the same over a sliding window of the last tokens plus
+ *                           the first (sink) tokens.
  *   oracle_kv_bytes      -- the pages' KV-memory closed form.
  *   codecs               -- bf16 / fp16 / OCP e4m3fn decoders, e4m3fn encoder.
  *
@@ -215,7 +217,7 @@ int oracle_kv_write(const int64_t* slot_mapping, int64_t num_tokens, const void*
 /* ---------------------------------------------------------- attention a2-a7 -- */
 
 /* Decode attention for the listed (sequence, query head) pairs:
- *   out[s][h][:] = softmax_t(scale * q[s][h] . K_t) @ V_t, t = 0 .. ctx[s]-1,
+ *   out[s][h][:] = softmax_t(scale * q[s][h] . K_t) @ V_t,  t in A(s),
  * where K_t, V_t are KV head g = h / G of token t, read at physical block
  * block_tables[s][t / B], offset t % B, and dequantised (fp8: code * scale).
  * ("Capitulo 2", section "Que guarda realmente el KV cache": Attn(q_t, [K_{1:t-1},
@@ -225,19 +227,30 @@ int oracle_kv_write(const int64_t* slot_mapping, int64_t num_tokens, const void*
  * the kernel walks the physical blocks in logical order; "KV cache: la memoria de
  * trabajo", section "Trucos para que el cuaderno sea mas fino": query heads in
  * groups of G share one K/V head.)
- * The softmax is the exact two-pass form: m = max z, w = exp(z - m), out = sum w V
- * / sum w, all fp64.  ctx = 0 gives zeros.  pairs == NULL means every (s, h) in
- * order; out is [num_pairs][d_h] fp64.  bytes_read (optional) accumulates the K/V
- * bytes this call decoded.  num_threads <= 0 lets OpenMP choose.
+ *
+ * A(s), the attended tokens of a context of n = ctx[s] tokens:
+ *   window == 0: every token, 0 .. n-1;
+ *   window >  0: the last `window` tokens, n - window .. n-1 ("PagedAttention por
+ *                dentro...", section "Sliding window attention": such models attend
+ *                only to the last K tokens), together with the first `sinks` tokens,
+ *                0 .. sinks-1 (same page, section "StreamingLLM...: los attention
+ *                sinks": keep the first 4 tokens plus a window of the last K).
+ * Tokens outside A(s) are never read, nor are their block-table entries.
+ * The softmax is the exact two-pass form over A(s): m = max z, w = exp(z - m),
+ * out = sum w V / sum w, all fp64.  ctx = 0 gives zeros.  pairs == NULL means every
+ * (s, h) in order; out is [num_pairs][d_h] fp64.  bytes_read (optional) accumulates
+ * the K/V bytes this call decoded.  num_threads <= 0 lets OpenMP choose.
  */
-int oracle_decode(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
-                  const void* k_cache, const void* v_cache, int cache_dtype, float k_scale,
-                  float v_scale, int64_t num_blocks, int32_t block_size, int32_t H_kv,
-                  int32_t d_h, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                  const int32_t* context_lens, float scale, const int32_t* pairs,
-                  int64_t num_pairs, double* out, int64_t* bytes_read, int num_threads) {
+int oracle_decode_window(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                         const void* k_cache, const void* v_cache, int cache_dtype, float k_scale,
+                         float v_scale, int64_t num_blocks, int32_t block_size, int32_t H_kv,
+                         int32_t d_h, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t window, int32_t sinks, float scale,
+                         const int32_t* pairs, int64_t num_pairs, double* out, int64_t* bytes_read,
+                         int num_threads) {
   if (H_kv <= 0 || num_q_heads % H_kv) return -4;
   if (!elem_bytes(q_dtype) || !elem_bytes(cache_dtype)) return -2;
+  if (window < 0 || sinks < 0) return -3;
   const int32_t G = num_q_heads / H_kv;
   const int cb = elem_bytes(cache_dtype);
   if (!pairs) num_pairs = (int64_t)num_seqs * num_q_heads;
@@ -255,42 +268,66 @@ int oracle_decode(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_he
     int32_t n = context_lens[s] - (MUT(6) ? 1 : 0);
     for (int32_t d = 0; d < d_h; ++d) o[d] = 0.0;
     if (n <= 0) continue;
+    /* the attended tokens, in logical order */
+    int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
     double* z = (double*)malloc(sizeof(double) * (size_t)n);
-    if (!z) { status = -7; continue; }
+    if (!tok || !z) { free(tok); free(z); status = -7; continue; }
+    int32_t na = 0;
+    for (int32_t t = 0; t < n; ++t) {
+      int in_window = MUT(9) ? t > n - window : t >= n - window;
+      int is_sink = MUT(10) ? 0 : t < sinks;
+      if (window == 0 || in_window || is_sink) tok[na++] = t;
+    }
     double qd_scale = MUT(4) ? 1.0 : (double)scale;
     double kscale = cache_dtype == O_FP8 ? (double)k_scale : 1.0;
     double vscale = cache_dtype == O_FP8 ? (double)v_scale : 1.0;
     const int64_t q_base = ((int64_t)s * num_q_heads + h) * d_h;
-    for (int32_t t = 0; t < n; ++t) {
+    for (int32_t j = 0; j < na; ++j) {
+      int32_t t = tok[j];
       int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
       int64_t row = ((phys * H_kv + g) * block_size + t % block_size) * d_h;
       double acc = 0.0;
       for (int32_t d = 0; d < d_h; ++d)
         acc += load_f64(q, q_base + d, q_dtype) *
                (load_f64(MUT(2) ? v_cache : k_cache, row + d, cache_dtype) * kscale);
-      z[t] = qd_scale * acc;
+      z[j] = qd_scale * acc;
       total_bytes += 2 * (int64_t)d_h * cb;
     }
     double m = z[0];
-    for (int32_t t = 1; t < n; ++t)
-      if (z[t] > m) m = z[t];
+    for (int32_t j = 1; j < na; ++j)
+      if (z[j] > m) m = z[j];
     double wsum = 0.0;
-    for (int32_t t = 0; t < n; ++t) {
-      z[t] = exp(z[t] - m);
-      wsum += z[t];
+    for (int32_t j = 0; j < na; ++j) {
+      z[j] = exp(z[j] - m);
+      wsum += z[j];
     }
-    for (int32_t t = 0; t < n; ++t) {
+    for (int32_t j = 0; j < na; ++j) {
+      int32_t t = tok[j];
       int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
       int64_t row = ((phys * H_kv + g) * block_size + t % block_size) * d_h;
       for (int32_t d = 0; d < d_h; ++d)
-        o[d] += z[t] * (load_f64(v_cache, row + d, cache_dtype) * vscale);
+        o[d] += z[j] * (load_f64(v_cache, row + d, cache_dtype) * vscale);
     }
     for (int32_t d = 0; d < d_h; ++d) o[d] /= wsum;
+    free(tok);
     free(z);
   }
   (void)num_blocks;
   if (bytes_read) *bytes_read += total_bytes;
   return status;
+}
+
+/* The whole context (no window): the plain decode step. */
+int oracle_decode(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                  const void* k_cache, const void* v_cache, int cache_dtype, float k_scale,
+                  float v_scale, int64_t num_blocks, int32_t block_size, int32_t H_kv,
+                  int32_t d_h, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, float scale, const int32_t* pairs,
+                  int64_t num_pairs, double* out, int64_t* bytes_read, int num_threads) {
+  return oracle_decode_window(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache_dtype,
+                              k_scale, v_scale, num_blocks, block_size, H_kv, d_h, block_tables,
+                              max_blocks_per_seq, context_lens, 0, 0, scale, pairs, num_pairs, out,
+                              bytes_read, num_threads);
 }
 
 int oracle_mutation(void) { return ORACLE_MUTATION; }

@@ -67,6 +67,14 @@ class Oracle:
                                       ctypes.c_int32, _i32p, ctypes.c_float, ctypes.c_void_p,
                                       ctypes.c_int64, _f64p, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.c_int]
+        lib.oracle_decode_window.restype = ctypes.c_int
+        lib.oracle_decode_window.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_float, ctypes.c_float, ctypes.c_int64,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                             ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, _f64p,
+                                             ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         lib.oracle_mutation.restype = ctypes.c_int
         self.mutation = lib.oracle_mutation()
 
@@ -118,7 +126,10 @@ class Oracle:
             raise ValueError(f"oracle_kv_write failed: {rc}")
 
     def decode(self, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, context_lens,
-               scale, k_scale=1.0, v_scale=1.0, pairs=None, threads=1, count_bytes=False):
+               scale, k_scale=1.0, v_scale=1.0, pairs=None, threads=1, count_bytes=False,
+               window=0, sinks=0):
+        """Attention of every (or each listed) (sequence, query head) pair; with
+        window > 0 only over the last `window` tokens plus the first `sinks`."""
         q = np.ascontiguousarray(q)
         n, hq, d = q.shape
         nb, hkv, bs, d2 = k_cache.shape
@@ -132,10 +143,11 @@ class Oracle:
             npairs, pptr = pairs.shape[0], pairs.ctypes.data
         out = np.zeros((npairs, d), dtype=np.float64)
         nbytes = ctypes.c_int64(0)
-        rc = self.lib.oracle_decode(q.ctypes.data, CODES[q_dtype], n, hq, k_cache.ctypes.data,
-                                    v_cache.ctypes.data, CODES[cache_dtype], k_scale, v_scale, nb,
-                                    bs, hkv, d, bt, bt.shape[1], cl, scale, pptr, npairs, out,
-                                    ctypes.byref(nbytes), threads)
+        rc = self.lib.oracle_decode_window(q.ctypes.data, CODES[q_dtype], n, hq, k_cache.ctypes.data,
+                                           v_cache.ctypes.data, CODES[cache_dtype], k_scale, v_scale,
+                                           nb, bs, hkv, d, bt, bt.shape[1], cl, int(window),
+                                           int(sinks), scale, pptr, npairs, out,
+                                           ctypes.byref(nbytes), threads)
         if rc:
             raise ValueError(f"oracle_decode failed: {rc}")
         if pairs is None:

@@ -48,13 +48,38 @@ def oracle_step(orc, w, threads: int = 1, pairs=None):
     return kc, vc, ns, out
 
 
-def dense_reference(w, s: int) -> np.ndarray:
-    """softmax(q K^T * scale) V per query head on sequence s's contiguous K/V (fp64, numpy).
+def attended_tokens(ctx: int, window: int = 0, sinks: int = 0) -> np.ndarray:
+    """Positions a decode of a ctx-token context attends to: all of them (window 0), else
+    the last `window` ones and the first `sinks` ones."""
+    t = np.arange(ctx)
+    if window == 0:
+        return t
+    return t[(t >= ctx - window) | (t < sinks)]
+
+
+def free_blocks_outside_window(w, window: int, sinks: int) -> np.ndarray:
+    """Block tables in which every block holding no attended token points at the
+    NaN-filled sentinel block, as if the engine had freed it."""
+    bt = w.block_tables.copy()
+    B = w.cfg.block_size
+    for s, ctx in enumerate(w.context_lens):
+        used = set((attended_tokens(int(ctx), window, sinks) // B).tolist())
+        for j in range((int(ctx) + B - 1) // B):
+            if j not in used:
+                bt[s, j] = w.sentinel_block
+    return bt
+
+
+def dense_reference(w, s: int, window: int = 0, sinks: int = 0) -> np.ndarray:
+    """softmax(q K^T * scale) V per query head on sequence s's contiguous K/V (fp64, numpy),
+    over the attended rows (all of them unless a window is given).
 
     Independent of the paged layout: K and V come in logical order from the
     generator; fp8 values go through torch's e4m3fn cast."""
     c = w.cfg
     k, v = w.logical_kv(s)
+    sel = attended_tokens(k.shape[0], window, sinks)
+    k, v = k[sel], v[sel]
     if c.kv_dtype == "fp8":
         kf = storage_to_f64(torch_fp8_quantise(k, c.src_dtype, w.k_scale), "fp8") * w.k_scale
         vf = storage_to_f64(torch_fp8_quantise(v, c.src_dtype, w.v_scale), "fp8") * w.v_scale

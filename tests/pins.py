@@ -14,7 +14,7 @@ from pathlib import Path
 import numpy as np
 import torch
 
-from helpers import dense_reference, oracle_step, storage_to_f64
+from helpers import dense_reference, free_blocks_outside_window, oracle_step, storage_to_f64
 from workloads import LLAMA8B, LONGCTX, PREFIX, R70B_FP8, TINY, make_workload
 
 GOLDEN = Path(__file__).resolve().parent / "golden"
@@ -228,7 +228,65 @@ def pin_half_codecs(orc):
         assert np.array_equal(r[~np.isnan(r)], g[~np.isnan(g)])
 
 
+# (window, sinks) cases: one token, within a block, a block, straddling blocks with 4
+# sinks (the pages' count), sinks reaching past the window start, a window wider than
+# any context.
+WINDOW_CASES = [(1, 0), (5, 0), (16, 0), (17, 4), (33, 4), (20, 30), (4096, 4)]
+
+
+def _decode_window(orc, w, kc, vc, window, sinks, tables=None):
+    c = w.cfg
+    return orc.decode(w.q, c.q_dtype, kc, vc, c.kv_dtype,
+                      w.block_tables if tables is None else tables, w.context_lens, w.scale,
+                      w.k_scale, w.v_scale, window=window, sinks=sinks)
+
+
+def pin_window_dense(orc):
+    """Windowed oracle == dense softmax over the explicitly selected rows (last `window`
+    tokens plus the first `sinks`) of the contiguous K/V."""
+    for name in ("llama8b", "r70b", "tiny", "mqa"):
+        w = make_workload(SMALL[name])
+        kc, vc, _, _ = oracle_step(orc, w)
+        for W, S in WINDOW_CASES:
+            out = _decode_window(orc, w, kc, vc, W, S)
+            for s in range(w.cfg.num_seqs):
+                err = np.abs(out[s] - dense_reference(w, s, W, S)).max()
+                assert err <= 1e-12, (name, W, S, s, err)
+
+
+def pin_window_one_is_last_value(orc):
+    """A one-token window (no sinks) attends to the new token alone: out == its V."""
+    w = make_workload(SMALL["llama8b"])
+    kc, vc, _, _ = oracle_step(orc, w)
+    out = _decode_window(orc, w, kc, vc, 1, 0)
+    v = storage_to_f64(w.new_v, "bf16")
+    G = w.cfg.group
+    for h in range(w.cfg.num_q_heads):
+        assert np.array_equal(out[:, h, :], v[:, h // G, :]), h
+
+
+def pin_window_covering_is_full(orc):
+    """A window as long as the context attends to everything: bit-identical to no window."""
+    w = make_workload(SMALL["r70b"])
+    kc, vc, _, full = oracle_step(orc, w)
+    for W, S in ((int(w.context_lens.max()), 0), (int(w.context_lens.max()) + 5, 4)):
+        assert np.array_equal(_decode_window(orc, w, kc, vc, W, S), full), (W, S)
+
+
+def pin_window_freed_blocks_unread(orc):
+    """Blocks holding no attended token may be freed (their table entries pointed at a
+    NaN-filled block): the windowed output is unchanged, bit for bit."""
+    w = make_workload(SMALL["llama8b"].replace(ctx_params=(60, 140)))
+    kc, vc, _, _ = oracle_step(orc, w)
+    for W, S in ((17, 4), (40, 0), (1, 16)):
+        ref = _decode_window(orc, w, kc, vc, W, S)
+        got = _decode_window(orc, w, kc, vc, W, S, free_blocks_outside_window(w, W, S))
+        assert np.isfinite(got).all() and np.array_equal(got, ref), (W, S)
+
+
 ALL_PINS = [pin_kv_bytes_golden, pin_block_addressing_golden, pin_dense_equivalence,
             pin_ctx1_returns_new_value, pin_equal_keys_mean_value, pin_zero_query_mean_value,
             pin_permutation_invariance, pin_gqa_head_mapping, pin_bytes_touched,
-            pin_write_placement, pin_fp8_codec, pin_fp8_saturation, pin_half_codecs]
+            pin_write_placement, pin_fp8_codec, pin_fp8_saturation, pin_half_codecs,
+            pin_window_dense, pin_window_one_is_last_value, pin_window_covering_is_full,
+            pin_window_freed_blocks_unread]
