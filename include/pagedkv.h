@@ -181,6 +181,27 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
                            size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode attention over a sliding window with attention sinks: each query head attends
+ * to the last `window` tokens of its context (the new token included) and to the first
+ * `sinks` tokens ("PagedAttention por dentro...", section "Sliding window attention":
+ * such models attend only to the last K tokens and the engine keeps only the blocks of
+ * the active window; section "StreamingLLM...: los attention sinks": the first 4
+ * tokens plus a window of the last K).  Every other argument, the workspace size and
+ * the schedules are those of paged_attention_decode, which is the window == 0 case.
+ *   window : >= 0; 0 = no window (every token, sinks ignored)
+ *   sinks  : >= 0; with window > 0, tokens 0 .. sinks-1 are attended as well
+ * Block-table entries of blocks holding no attended token are never read (they may
+ * name freed blocks).  Returns PKV_ERR_SHAPE for a negative window or sink count.
+ */
+int paged_attention_decode_window(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
+                                  int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                  const pkv_cache_desc* cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t window, int32_t sinks, float scale,
+                                  void* out, pkv_dtype out_dtype, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Decode attention for a batch in which groups of sequences share a prefix of physical
  * blocks -- prefix caching: their block tables point at the same refcounted blocks
  * ("La despensa por casilleros", section "Prefix caching: compartir casilleros con

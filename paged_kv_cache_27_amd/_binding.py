@@ -23,7 +23,7 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHA
           -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH"}
 
 EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_schedule",
-            "paged_attention_workspace_size", "paged_attention_decode",
+            "paged_attention_workspace_size", "paged_attention_decode", "paged_attention_decode_window",
             "paged_attention_shared_prefix_workspace_size", "paged_attention_decode_shared_prefix",
             "pkv_status_string", "pkv_abi_version"]
 SCHEDULES = {0: "single-pass", 1: "fixed-partitions", 2: "balanced"}
@@ -74,6 +74,10 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.POINTER(CacheDesc), vp, i32, vp, i32, f32, vp,
                                            ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_window.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp,
+                                                  ctypes.POINTER(CacheDesc), vp, i32, vp, i32, i32, i32,
+                                                  f32, vp, ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
+    lib.paged_attention_decode_window.restype = ctypes.c_int
     lib.paged_attention_shared_prefix_workspace_size.argtypes = [ctypes.POINTER(CacheDesc), ctypes.c_int,
                                                                  i32, i32, i32, i32, i32, i32]
     lib.paged_attention_shared_prefix_workspace_size.restype = ctypes.c_size_t
@@ -217,6 +221,37 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                _ptr(q), qd, n, hq,
                _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
                block_tables.shape[1], _ptr(context_lens), int(max_context_len), float(scale),
+               _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
+               int(partition_size), _ptr(workspace) if workspace is not None else None,
+               workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def paged_attention_decode_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  scale: float, out: torch.Tensor, max_context_len: int,
+                                  window: int, sinks: int = 0, partition_size: int = 0,
+                                  workspace: torch.Tensor | None = None, kv_dtype=None,
+                                  k_scale: float = 1.0, v_scale: float = 1.0, q_dtype=None,
+                                  out_dtype=None, shared_blocks: bool = False,
+                                  stream=None) -> torch.Tensor:
+    """Decode attention into `out` over the last `window` tokens of each context plus its
+    first `sinks` (window 0: every token).  Other arguments as paged_attention_decode."""
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale, shared_blocks)
+    n, hq, d = q.shape
+    qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
+    if workspace is None:
+        need = paged_attention_workspace_size(desc, qd, n, hq, max_context_len, partition_size)
+        if need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    _check("paged_attention_decode_window",
+           lib.paged_attention_decode_window(
+               _ptr(q), qd, n, hq,
+               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
+               block_tables.shape[1], _ptr(context_lens), int(max_context_len), int(window),
+               int(sinks), float(scale),
                _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
                int(partition_size), _ptr(workspace) if workspace is not None else None,
                workspace.numel() if workspace is not None else 0, _stream(stream)))

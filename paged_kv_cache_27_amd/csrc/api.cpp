@@ -140,7 +140,7 @@ int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 3; }
+int32_t pkv_abi_version(void) { return 4; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -228,8 +228,22 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
                            int32_t max_context_len, float scale, void* out,
                            pkv_dtype out_dtype, int32_t partition_size, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
+  return paged_attention_decode_window(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
+                                       block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                                       0, 0, scale, out, out_dtype, partition_size, workspace,
+                                       workspace_bytes, stream);
+}
+
+int paged_attention_decode_window(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
+                                  int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                  const pkv_cache_desc* cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t window, int32_t sinks, float scale,
+                                  void* out, pkv_dtype out_dtype, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_decode_shape(cache, q_dtype, out_dtype, num_seqs, num_q_heads, max_context_len);
   if (st) return st;
+  if (window < 0 || sinks < 0) return PKV_ERR_SHAPE;
   if (max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
@@ -263,6 +277,8 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
   a.context_lens = context_lens;
   a.max_context_len = max_context_len;
   a.scale = scale;
+  a.window = window;
+  a.sinks = window > 0 ? sinks : 0;
   a.out = out;
   a.out_dtype = out_dtype;
   a.partition = plan.partition;
@@ -369,6 +385,8 @@ int paged_attention_decode_shared_prefix(
   a.context_lens = context_lens;
   a.max_context_len = max_context_len;
   a.scale = scale;
+  a.window = 0;
+  a.sinks = 0;
   a.out = out;
   a.out_dtype = out_dtype;
   a.partition = 0;

@@ -44,7 +44,13 @@ decode_kernel(const DecodeArgs a) {
   wd.init(a, lds_p[wv], lds_alpha[wv]);
   wd.begin(a, s, g, ctx);
   // Partitions are multiples of 16 tokens, so chunks never straddle two partitions.
-  run_chunks(wd, tok_begin / 16 + wv, (tok_end + 15) / 16, NW);
+  // The partition's chunks, without those outside a window's attended ranges (in the
+  // gap-free numbering of run_chunks; a partition wholly in the gap has none and
+  // leaves a neutral partial).
+  int ca, cw;
+  attended_chunks(ctx, a.window, a.sinks, ca, cw);
+  auto gapless = [&](int c) { return c < ca ? c : (c < cw ? ca : c - (cw - ca)); };
+  run_chunks(wd, gapless(tok_begin / 16) + wv, gapless((tok_end + 15) / 16), NW, ca, cw - ca);
 
   wd.finish();
   wd.visit([&](int h, int d, float v) { lds_acc[wv][h * D + d] = v; });

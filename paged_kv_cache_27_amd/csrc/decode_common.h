@@ -207,6 +207,7 @@ struct ValuDecoder {
   const uint8_t* vc;
   const int32_t* bt;
   int BS, Hkv, G, g, tok_end;
+  int win_lo, sink_hi;  // attended: tokens >= win_lo or < sink_hi (and < tok_end)
 
   __device__ __forceinline__ void init(const DecodeArgs& a, float* p_tile, float* alpha_tile) {
     lane = threadIdx.x & 63;
@@ -225,6 +226,8 @@ struct ValuDecoder {
   __device__ __forceinline__ void begin(const DecodeArgs& a, int s, int g_, int ctx) {
     g = g_;
     tok_end = ctx;
+    win_lo = a.window > 0 ? ctx - a.window : 0;
+    sink_hi = a.window > 0 ? min(a.sinks, ctx) : 0;
     bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
     const int hrow = lane & 15;
     const bool qvalid = hrow < G;
@@ -245,6 +248,8 @@ struct ValuDecoder {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
   }
+
+  __device__ __forceinline__ bool keep(int t) const { return t < tok_end && (t >= win_lo || t < sink_hi); }
 
   // Physical block of chunk c (tokens 16c ..), a scalar load: the index is uniform,
   // and the scalar path keeps table reads out of the vector-memory counter.
@@ -277,7 +282,7 @@ struct ValuDecoder {
 #pragma unroll
       for (int j = 0; j < T::SUB; ++j) S = T::mma(qf[c2 * T::SUB + j], T::kfrag(buf.k[c2], j), S);
     // S[r] = score of head 4*grp + r against token ct + lane%16.
-    const bool tok_ok = ct + (lane & 15) < tok_end;
+    const bool tok_ok = keep(ct + (lane & 15));
     float pr[NR], alpha[NR];
     bool changed = false;
 #pragma unroll
@@ -315,7 +320,7 @@ struct ValuDecoder {
       const int t = i * RPI + lane / LPR;
       float vf[8];
       Unpack8<KV>::run(buf.v[i].w, vf);
-      if (ct + t >= tok_end) {  // tail of the last block: never let its bytes in
+      if (!keep(ct + t)) {  // past the context or outside the window: never let its bytes in
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[e] = 0.0f;
       }
@@ -490,6 +495,7 @@ struct MfmaDecoder {
   const uint8_t* vc;
   const int32_t* bt;
   int BS, Hkv, G, g, tok_end;
+  int win_lo, sink_hi;  // attended: tokens >= win_lo or < sink_hi (and < tok_end)
 
   __device__ __forceinline__ void init(const DecodeArgs& a, float*, float*) {
     lane = threadIdx.x & 63;
@@ -505,6 +511,8 @@ struct MfmaDecoder {
   __device__ __forceinline__ void begin(const DecodeArgs& a, int s, int g_, int ctx) {
     g = g_;
     tok_end = ctx;
+    win_lo = a.window > 0 ? ctx - a.window : 0;
+    sink_hi = a.window > 0 ? min(a.sinks, ctx) : 0;
     bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
     const int grp = lane >> 4;
     const uint8_t* qbase = (const uint8_t*)a.q + ((size_t)s * a.num_q_heads + (size_t)g * G) * D * QB;
@@ -524,6 +532,8 @@ struct MfmaDecoder {
       for (int hf = 0; hf < HALVES; ++hf) acc[hs][hf] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
+
+  __device__ __forceinline__ bool keep(int t) const { return t < tok_end && (t >= win_lo || t < sink_hi); }
 
   __device__ __forceinline__ int table_entry(int c) const {
     const int idx = __builtin_amdgcn_readfirstlane((16 * c) / BS);
@@ -572,12 +582,12 @@ struct MfmaDecoder {
         for (int hs = 0; hs < HS; ++hs) S[hs] = T::mma(kf, qf[hs][c2 * T::SUB + j], S[hs]);
       }
     const int tb = ct + (lane >> 4);
-    if (ct + 16 > tok_end) {
-      // last chunk of the context: rows past it are never let in (their bytes may
-      // be anything, NaN included)
+    if (ct + 16 > tok_end || ct < win_lo) {
+      // last chunk of the context, or a chunk only partly attended: rows not attended
+      // are never let in (their bytes may be anything, NaN included)
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (tb + 4 * k >= tok_end) {
+        if (!keep(tb + 4 * k)) {
 #pragma unroll
           for (int w = 0; w < VW; ++w) buf.v[k][w] = 0u;
         }
@@ -589,7 +599,7 @@ struct MfmaDecoder {
     for (int hs = 0; hs < HS; ++hs) {
       float s[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s[k] = tb + 4 * k < tok_end ? S[hs][k] * scale_l2 : kNegInf;
+      for (int k = 0; k < 4; ++k) s[k] = keep(tb + 4 * k) ? S[hs][k] * scale_l2 : kNegInf;
       float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       bm = xor32_max(xor16_max(bm));
       const float mn = fmaxf(m[hs], bm);
@@ -669,6 +679,33 @@ template <int KV, int Q, int D, int GP, bool NT>
 using Decoder = typename std::conditional<KV == kF32, ValuDecoder<KV, Q, D, GP, NT>,
                                           MfmaDecoder<KV, Q, D, GP, NT>>::type;
 
+// The 16-token chunks of a ctx-token context that hold attended tokens: [0, a) and
+// [b, nc) with a <= b, nc = ceil(ctx / 16).  Without a window (window == 0) or when the
+// window reaches back to the sink tokens, one range: a = b = nc.  With a window, the
+// sink chunks [0, ceil(min(sinks, ctx) / 16)) and the window chunks from
+// floor((ctx - window) / 16) ("PagedAttention por dentro...", sections "Sliding window
+// attention" and "StreamingLLM...: los attention sinks": the last K tokens plus the
+// first few).  Chunks in the gap are never read: their blocks may have been freed.
+__device__ __forceinline__ void attended_chunks(int ctx, int window, int sinks, int& a, int& b) {
+  const int nc = (ctx + 15) >> 4;
+  a = nc;
+  b = nc;
+  if (window > 0 && ctx - window > 0) {
+    const int sa = (min(sinks, ctx) + 15) >> 4;
+    const int wb = (ctx - window) >> 4;
+    if (sa < wb) {
+      a = sa;
+      b = wb;
+    }
+  }
+}
+// Attended chunks of a context, counted without the gap.
+__device__ __forceinline__ int attended_chunk_count(int ctx, int window, int sinks) {
+  int a, b;
+  attended_chunks(ctx, window, sinks, a, b);
+  return a + ((ctx + 15) >> 4) - b;
+}
+
 // Chunks c_begin, c_begin + step, ... < c_end (chunk c covers tokens 16c .. 16c+15),
 // with the loads of the next W::kDepth chunks in flight while one is computed
 // (kDepth + 1 register buffers, rotated by a fully unrolled inner loop).  Every step
@@ -676,12 +713,19 @@ using Decoder = typename std::conditional<KV == kF32, ValuDecoder<KV, Q, D, GP, 
 // buffer resource, which read nothing -- so the vector-memory wait before a chunk's
 // use only covers that chunk's own loads, never the ones issued after it.
 // Block-table entries come one chunk ahead through the scalar path.
+//
+// The range is in gap-free chunk numbers v (see attended_chunks): chunk v + shift is
+// read when v >= split, chunk v otherwise.
 template <class W>
-__device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int step) {
+__device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int step, int split = 0x7fffffff,
+                                           int shift = 0) {
   constexpr int DEPTH = W::kDepth;
   if (c_begin >= c_end) return;
   const int n = (c_end - c_begin + step - 1) / step;  // chunks of this wave
-  auto chunk = [&](int i) { return c_begin + (i < n ? i : n - 1) * step; };
+  auto chunk = [&](int i) {
+    const int v = c_begin + (i < n ? i : n - 1) * step;
+    return v >= split ? v + shift : v;
+  };
   typename W::Buf buf[DEPTH + 1];
   int blk = wd.table_entry(chunk(0));
 #pragma unroll

@@ -147,10 +147,11 @@ decode_sk_kernel(const DecodeArgs a) {
   // ---- exclusive prefix of per-sequence chunk counts, in LDS ----
   const int per = (N + NTH - 1) / NTH;
   const int i0s = min(N, tid * per), i1s = min(N, i0s + per);
-  // chunks of sequence i this kernel streams (after its shared prefix when PRE)
+  // chunks of sequence i this kernel streams: its attended chunks (all of them without
+  // a window), after its shared prefix when PRE (which takes no window)
   auto chunks_of = [&](int i) {
-    const int n = (a.context_lens[i] + 15) >> 4;
-    return PRE ? max(0, n - (a.seq_begin[i] >> 4)) : n;
+    if constexpr (PRE) return max(0, ((a.context_lens[i] + 15) >> 4) - (a.seq_begin[i] >> 4));
+    return attended_chunk_count(a.context_lens[i], a.window, a.sinks);
   };
   int local = 0;
   for (int i = i0s; i < i1s; ++i) local += chunks_of(i);
@@ -267,9 +268,16 @@ decode_sk_kernel(const DecodeArgs a) {
   // Units [u0, u1) of segment X.
   auto do_piece = [&](const Seg& X, long long u0, long long u1) {
     const int cb = (int)(u0 - X.xs), ce = (int)(u1 - X.xs);
-    const int cb0 = PRE ? (a.seq_begin[X.s] >> 4) : 0;  // first streamed chunk of the context
-    wd.begin(a, X.s, X.g, a.context_lens[X.s]);
-    run_chunks(wd, cb0 + cb, cb0 + ce, 1);
+    const int ctx = a.context_lens[X.s];
+    wd.begin(a, X.s, X.g, ctx);
+    if constexpr (PRE) {
+      const int cb0 = a.seq_begin[X.s] >> 4;  // first streamed chunk of the context
+      run_chunks(wd, cb0 + cb, cb0 + ce, 1);
+    } else {
+      int ca, cw;  // attended chunks [0, ca) and [cw, ...): units count them without the gap
+      attended_chunks(ctx, a.window, a.sinks, ca, cw);
+      run_chunks(wd, cb, ce, 1, __builtin_amdgcn_readfirstlane(ca), __builtin_amdgcn_readfirstlane(cw - ca));
+    }
     wd.finish();
     float Mh[GP], Lh[GP];
 #pragma unroll

@@ -34,6 +34,9 @@ struct DecodeArgs {
   const int32_t* context_lens;
   int32_t max_context_len;
   float scale;
+  // sliding window with attention sinks: window > 0 attends to the last `window`
+  // tokens of each context and its first `sinks`; window == 0 to every token
+  int32_t window, sinks;
   void* out;
   int out_dtype;
   int32_t partition;       // tokens per partition (> 0)

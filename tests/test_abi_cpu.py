@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pkv.pkv_abi_version() == 3
+    assert pkv.pkv_abi_version() == 4
 
 
 def test_workspace_header_constant_matches_header():
@@ -75,6 +75,21 @@ def test_decode_argument_errors():
     assert need > 0
     assert _decode(lib, _desc(), maxb=40, maxctx=600, part=32, ws=FAKE, wsb=need - 1) == -5
     assert _decode(lib, _desc(), n=0) == 0  # empty batch: nothing to do
+
+
+def _decode_window(lib, desc, window, sinks, n=2, q=FAKE):
+    return lib.paged_attention_decode_window(q, pkv.BF16, n, 4, FAKE, FAKE, ctypes.byref(desc), FAKE, 4,
+                                             FAKE, 40, window, sinks, 0.1, FAKE, pkv.BF16, 0, None, 0,
+                                             None)
+
+
+def test_window_argument_errors():
+    lib = pkv.load_library()
+    assert _decode_window(lib, _desc(), -1, 0) == -3
+    assert _decode_window(lib, _desc(), 16, -4) == -3
+    assert _decode_window(lib, _desc(head_dim=96), 16, 4) == -3  # the decode checks still apply
+    assert _decode_window(lib, _desc(), 16, 4, q=None) == -1
+    assert _decode_window(lib, _desc(), 16, 4, n=0) == 0
 
 
 def test_workspace_sizes_and_schedules():

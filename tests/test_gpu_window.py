@@ -1,0 +1,120 @@
+"""Sliding-window decode with attention sinks vs the oracle, through the C ABI (GPU only).
+
+Before each windowed decode the blocks holding no attended token are freed: their
+table entries are pointed at the NaN-filled sentinel block, on both sides, so a kernel
+that let any of their bytes in would fail.  The bar is the decode bar (4e-3, fp8 KV
+2e-2, times max(1, |ref|)), element by element, in all three schedules.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_27_amd as pkv
+from gpu_helpers import GpuStep, assert_close_to_oracle, out_to_f64
+from helpers import free_blocks_outside_window, oracle_step
+from pins import SMALL, WINDOW_CASES
+from workloads import LONGCTX, R70B_FP8, make_workload
+
+pytestmark = pytest.mark.gpu
+THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.load_library()
+
+
+def _decode_window(g, window, sinks, tables, partition):
+    w = g.w
+    out = torch.empty_like(g.out)
+    pkv.paged_attention_decode_window(g.q, g.k_cache, g.v_cache, tables, g.context_lens, w.scale, out,
+                                      w.max_context_len, window, sinks, partition_size=partition,
+                                      kv_dtype=g.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale,
+                                      shared_blocks=bool(w.shared_blocks))
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_window(orc, w, kc, vc, window, sinks, tables):
+    c = w.cfg
+    return orc.decode(w.q, c.q_dtype, kc, vc, c.kv_dtype, tables, w.context_lens, w.scale, w.k_scale,
+                      w.v_scale, window=window, sinks=sinks, threads=THREADS)
+
+
+def _prepared(cfg):
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    return w, g
+
+
+@pytest.mark.parametrize("name", ["llama8b", "r70b", "tiny", "mqa", "mha-f16", "longctx", "prefix"])
+def test_window_small_all_schedules(orc, name):
+    w, g = _prepared(SMALL[name])
+    kc, vc, _, _ = oracle_step(orc, w)
+    B = w.cfg.block_size
+    for W, S in WINDOW_CASES:
+        bt = free_blocks_outside_window(w, W, S)
+        ref = _oracle_window(orc, w, kc, vc, W, S, bt)
+        tables = torch.from_numpy(bt).cuda()
+        for part in (0, -1, 2 * B):
+            print(f"window case {name} W={W} S={S} partition={part}", flush=True)
+            out = out_to_f64(_decode_window(g, W, S, tables, part))
+            assert_close_to_oracle(out, ref, w.cfg.kv_dtype, f"{name} W={W} S={S} part={part}")
+
+
+@pytest.mark.parametrize("name", ["llama8b", "r70b", "tiny"])
+def test_window_covering_context_is_bit_identical(name):
+    """A window as long as every context attends to everything: the very same bits as
+    paged_attention_decode in the same schedule."""
+    w, g = _prepared(SMALL[name])
+    W = int(w.context_lens.max())
+    for part in (0, -1, 2 * w.cfg.block_size):
+        full = g.decode(part).clone()
+        torch.cuda.synchronize()
+        for S in (0, 4):
+            got = _decode_window(g, W, S, g.block_tables, part)
+            assert torch.equal(got, full), (name, part, S)
+
+
+def test_window_zero_is_plain_decode():
+    w, g = _prepared(SMALL["llama8b"])
+    full = g.decode(0).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(_decode_window(g, 0, 7, g.block_tables, 0), full)
+
+
+def test_window_ragged_edges(orc):
+    """Window and sink edges on every side of a block boundary, over contexts that end
+    anywhere in a block (one sequence per length 1 .. 70)."""
+    cfg = SMALL["llama8b"].replace(num_seqs=70, ctx_kind="fixed", ctx_params=tuple(range(1, 71)))
+    w, g = _prepared(cfg)
+    kc, vc, _, _ = oracle_step(orc, w)
+    for W, S in ((15, 0), (16, 1), (17, 15), (31, 16), (32, 17), (48, 33), (2, 40)):
+        bt = free_blocks_outside_window(w, W, S)
+        ref = _oracle_window(orc, w, kc, vc, W, S, bt)
+        tables = torch.from_numpy(bt).cuda()
+        for part in (0, -1, 16):
+            print(f"ragged window W={W} S={S} partition={part}", flush=True)
+            out = out_to_f64(_decode_window(g, W, S, tables, part))
+            assert_close_to_oracle(out, ref, "bf16", f"W={W} S={S} part={part}")
+
+
+@pytest.mark.parametrize("cfg,window,sinks,part", [(LONGCTX, 4096, 4, 0), (LONGCTX, 4096, 4, 512),
+                                                    (R70B_FP8, 1000, 4, 0)],
+                         ids=["longctx-4096-balanced", "longctx-4096-p512", "70b-fp8-1000"])
+def test_window_full_size(orc, cfg, window, sinks, part):
+    """Full-size workloads with a Mistral-style window (the last 4096 tokens) and the
+    pages' 4 sink tokens: every output against the oracle, freed blocks poisoned."""
+    print(f"full-size window case {cfg.name} W={window} S={sinks} partition={part}", flush=True)
+    w, g = _prepared(cfg)
+    bt = free_blocks_outside_window(w, window, sinks)
+    out = out_to_f64(_decode_window(g, window, sinks, torch.from_numpy(bt).cuda(), part))
+    del g
+    kc, vc, _, _ = oracle_step(orc, w, pairs=np.zeros((0, 2), np.int32))
+    ref = _oracle_window(orc, w, kc, vc, window, sinks, bt)
+    assert_close_to_oracle(out, ref, w.cfg.kv_dtype, cfg.name)
