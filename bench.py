@@ -63,13 +63,21 @@ def parse_args():
 
 
 def pick_config(spec):
-    from workloads import CONFIGS
+    from workloads import CONFIGS, EXTRA_CONFIGS
     if str(spec).isdigit():
         return CONFIGS[int(spec) - 1]
-    for c in CONFIGS:
+    for c in CONFIGS + EXTRA_CONFIGS:
         if c.name == spec:
             return c
-    raise SystemExit(f"unknown workload {spec}; known: {[c.name for c in CONFIGS]}")
+    raise SystemExit(f"unknown workload {spec}; known: {[c.name for c in CONFIGS + EXTRA_CONFIGS]}")
+
+
+def window_tokens(ctx, window, sinks):
+    """Positions a decode over a sliding window attends to: the last `window` of a
+    ctx-token context plus its first `sinks` (every position when window is 0)."""
+    import numpy as np
+    t = np.arange(int(ctx))
+    return t if window == 0 else t[(t >= ctx - window) | (t < sinks)]
 
 
 def algorithmic_bytes(w):
@@ -80,8 +88,13 @@ def algorithmic_bytes(w):
     c = w.cfg
     n, hq, hkv, d, B = c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size
     ctx = w.context_lens.astype("int64")
-    kv = int(ctx.sum()) * hkv * d * 2 * DT_BYTES[c.kv_dtype]
-    table = int(((ctx + B - 1) // B).sum()) * 4 + 4 * n
+    if c.window:  # only the attended tokens and the table entries of their blocks
+        att = [window_tokens(x, c.window, c.sinks) for x in ctx]
+        kv = sum(len(a) for a in att) * hkv * d * 2 * DT_BYTES[c.kv_dtype]
+        table = sum(len(set((a // B).tolist())) for a in att) * 4 + 4 * n
+    else:
+        kv = int(ctx.sum()) * hkv * d * 2 * DT_BYTES[c.kv_dtype]
+        table = int(((ctx + B - 1) // B).sum()) * 4 + 4 * n
     qo = n * hq * d * (DT_BYTES[c.q_dtype] + DT_BYTES[c.out_dtype])
     decode = kv + table + qo
     write = n * hkv * d * 2 * (DT_BYTES[c.src_dtype] + DT_BYTES[c.kv_dtype]) + 8 * n
@@ -159,6 +172,17 @@ class Step:
                                w.k_scale, w.v_scale)
             torch.cuda.synchronize()
             del hk, hv, hs, hp, hslots
+        # A sliding window: the engine frees every block holding no attended token; its
+        # table entries then name a NaN-filled block the decode must never let in.
+        if c.window:
+            bt = w.block_tables.copy()
+            for s, x in enumerate(w.context_lens):
+                used = set((window_tokens(x, c.window, c.sinks) // c.block_size).tolist())
+                for j in range((int(x) + c.block_size - 1) // c.block_size):
+                    if j not in used:
+                        bt[s, j] = w.sentinel_block
+            self.block_tables = torch.from_numpy(bt).to(dev)
+            self.schedule = dict(self.schedule, window=c.window, sinks=c.sinks)
 
     def slot_map(self):
         self.pkv.paged_kv_slot_mapping(self.new_seq, self.new_pos, self.block_tables,
@@ -176,6 +200,13 @@ class Step:
             self.pkv.paged_attention_decode_shared_prefix(
                 self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, w.scale,
                 self.out, w.max_context_len, starts, plens, gmax, pmax, workspace=self.pworkspace)
+            return
+        if w.cfg.window:
+            self.pkv.paged_attention_decode_window(
+                self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, w.scale,
+                self.out, w.max_context_len, w.cfg.window, w.cfg.sinks, partition_size=self.partition,
+                workspace=self.workspace, kv_dtype=self.kv_dtype, k_scale=w.k_scale,
+                v_scale=w.v_scale, shared_blocks=self.shared)
             return
         self.pkv.paged_attention_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
                                         self.context_lens, w.scale, self.out, w.max_context_len,
@@ -195,6 +226,13 @@ KERNEL_LABEL = {
     "single-pass": "paged_attention_decode call (decode_kernel)",
     "shared-prefix": "paged_attention_decode_shared_prefix call (prefix_kernel + decode_sk_kernel suffix pass)",
 }
+
+
+def kernel_label(schedule):
+    label = KERNEL_LABEL.get(schedule["schedule"], "?")
+    if schedule.get("window"):
+        label = label.replace("paged_attention_decode call", "paged_attention_decode_window call")
+    return label
 
 
 def traffic_for(cfg_name):
@@ -277,6 +315,49 @@ def measure(cfg, args, partition=None):
     return w, st, res
 
 
+def measure_block_moves(args):
+    """Copy-on-write copies and swap-outs of whole blocks on the 8B-shaped layer's cache:
+    algorithmic bytes = blocks x block bytes x (K, V) x (read + write), cold L2/MALL."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_27_amd as pkv
+    from workloads import LLAMA8B, cache_shape, make_workload
+
+    w = make_workload(LLAMA8B)
+    shape = cache_shape(w)
+    k = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    block_bytes = k[0].numel() * 2
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(w.num_blocks).astype(np.int32)
+    n = min(2048, w.num_blocks // 2)
+    src = torch.from_numpy(perm[:n].copy()).cuda()
+    dst = torch.from_numpy(perm[n:2 * n].copy()).cuda()
+    kb = torch.empty((n,) + tuple(shape[1:]), dtype=torch.bfloat16, device="cuda")
+    vb = torch.empty_like(kb)
+    flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    out = {}
+    for name, call in (("copy_blocks", lambda: pkv.paged_kv_copy_blocks(src, dst, k, v)),
+                       ("swap_out_to_device", lambda: pkv.paged_kv_swap_out(src, k, v, kb, vb))):
+        for _ in range(3):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.reps)]
+        for e0, e1 in ev:
+            sink.copy_(flush.sum())
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        nbytes = n * block_bytes * 2 * 2
+        out[name] = {"blocks": n, "block_bytes": block_bytes, "bytes": nbytes, "ms_cold_mean": ms,
+                     "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[block moves] {name}: {n} blocks of {block_bytes} B (K and V), {ms * 1e3:.1f} us, "
+            f"{out[name]['GBps']:.0f} GB/s read+write ({100 * out[name]['frac_hbm_peak']:.1f}% of peak)")
+    return out
+
+
 def cpu_baseline(w, budget_s):
     """The fp64 oracle on this host's cores over whole sequences (all query heads), taken
     in order until the wall budget is spent."""
@@ -303,9 +384,10 @@ def cpu_baseline(w, budget_s):
             pairs = np.array([(s, h) for s in seqs for h in range(c.num_q_heads)], np.int32)
             t0 = time.perf_counter()
             orc.decode(w.q, c.q_dtype, kc, vc, c.kv_dtype, w.block_tables, w.context_lens,
-                       w.scale, w.k_scale, w.v_scale, pairs=pairs, threads=threads)
+                       w.scale, w.k_scale, w.v_scale, pairs=pairs, threads=threads,
+                       window=c.window, sinks=c.sinks)
             elapsed += time.perf_counter() - t0
-            tokens += int(w.context_lens[list(seqs)].sum())
+            tokens += sum(len(window_tokens(w.context_lens[s], c.window, c.sinks)) for s in seqs)
             seq_heads += len(seqs) * c.num_q_heads
             s0 = seqs[-1] + 1
         passes += s0 / c.num_seqs
@@ -345,13 +427,14 @@ def main():
     torch.cuda.empty_cache()
     others = []
     if args.all:
-        from workloads import CONFIGS
-        for c in CONFIGS:
+        from workloads import CONFIGS, EXTRA_CONFIGS
+        for c in CONFIGS + EXTRA_CONFIGS:
             if c.name != cfg.name:
                 _, s2, r2 = measure(c, args)
                 others.append(r2)
                 del s2
                 torch.cuda.empty_cache()
+    blocks = measure_block_moves(args) if args.all else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -368,20 +451,21 @@ def main():
                    "block_size": c.block_size, "q_dtype": c.q_dtype, "kv_dtype": c.kv_dtype,
                    "context_lens": f"{c.ctx_kind}{tuple(c.ctx_params)}",
                    "sum_context": res["sum_context"], "schedule": res["schedule"],
-                   "seed": c.seed},
+                   "seed": c.seed, **({"window": c.window, "sinks": c.sinks} if c.window else {})},
         "pct_hbm_peak": round(100 * res["step_GBps"] / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(res["seq_heads_per_s"], 1),
         "roofline": {"bound": "hbm", "achieved": round(res["decode_GBps_cold"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["decode_frac_hbm_peak"], 4), "traffic": traffic,
-                     "kernel": KERNEL_LABEL.get(res["schedule"]["schedule"], "?"),
+                     "kernel": kernel_label(res["schedule"]),
                      "bytes_per_launch": res["bytes"]["decode"],
                      "mean_launch_ms": round(res["decode_ms_cold_mean"], 6)},
         "cpu_baseline": cpu,
     }
     if args.json_out:
         Path(args.json_out).parent.mkdir(parents=True, exist_ok=True)
-        Path(args.json_out).write_text(json.dumps({"headline": res, "others": others, "cpu": cpu}, indent=1))
+        Path(args.json_out).write_text(json.dumps({"headline": res, "others": others, "block_moves": blocks,
+                                                   "cpu": cpu}, indent=1))
     print(json.dumps(line), flush=True)
 
 

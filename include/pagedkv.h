@@ -55,7 +55,9 @@ typedef enum {
   PKV_ERR_SHAPE = -3,       /* unsupported head_dim / block_size / group size, or bad sizes */
   PKV_ERR_HEADS = -4,       /* num_q_heads is not a multiple of num_kv_heads */
   PKV_ERR_WORKSPACE = -5,   /* workspace too small, or bad partition size */
-  PKV_ERR_LAUNCH = -6       /* the HIP runtime reported an error at launch */
+  PKV_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
+  PKV_ERR_POOL_EXHAUSTED = -7, /* block pool: fewer free blocks than asked for */
+  PKV_ERR_BLOCK_STATE = -8  /* block pool: a block ID out of range, or not allocated */
 } pkv_status;
 
 /* Every non-empty decode workspace starts with this many bytes of arrival counters,
@@ -245,6 +247,65 @@ int paged_attention_decode_shared_prefix(
     const int32_t* group_starts, int32_t num_groups, int32_t max_group_size, const int32_t* prefix_lens,
     int32_t max_prefix_len, float scale, void* out, pkv_dtype out_dtype, void* workspace,
     size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- block moves ---
+ * Whole physical blocks of one layer's K and V caches (block_bytes = num_kv_heads *
+ * block_size * head_dim * element bytes each).  IDs are int32 device arrays; a
+ * negative ID skips its pair or row.  Asynchronous on `stream`; no allocation.
+ *
+ * Copy-on-write: block src_ids[i] -> block dst_ids[i] in both caches, so a sequence
+ * about to write into a block it shares gets a private copy first ("PagedAttention por
+ * dentro...", section "Copy-on-write para sampling paralelo": only the last affected
+ * block is copied; "La despensa por casilleros", section "Prefix caching...": the block
+ * manager copies the block for that branch and only then writes).
+ * Precondition (unchecked): destination IDs are distinct from each other and from
+ * every source ID (as fresh blocks from pkv_pool_cow are).
+ */
+int paged_kv_copy_blocks(const int32_t* src_ids, const int32_t* dst_ids, int32_t num_pairs,
+                         void* k_cache, void* v_cache, const pkv_cache_desc* cache, hipStream_t stream);
+
+/*
+ * Swap out: block ids[i] of each cache -> row i of k_buf / v_buf ([num][block_bytes]);
+ * swap in: row i -> block ids[i].  ("PagedAttention por dentro...", section
+ * "Estrategia 2: swap": an evicted session's blocks move to CPU RAM and back to VRAM
+ * when it resumes.)  The buffers may be device memory or pinned host memory
+ * (hipHostMalloc); 16-byte aligned.  Release the swapped-out blocks to the pool only
+ * after the stream has finished the swap out, and decode from swapped-in blocks only
+ * on the same stream after the swap in (or after synchronising with it).
+ */
+int paged_kv_swap_out(const int32_t* ids, int32_t num, const void* k_cache, const void* v_cache,
+                      const pkv_cache_desc* cache, void* k_buf, void* v_buf, hipStream_t stream);
+int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const void* v_buf,
+                     void* k_cache, void* v_cache, const pkv_cache_desc* cache, hipStream_t stream);
+
+/* ----------------------------------------------------------------- block pool ---
+ * Host-side refcounted free list of one cache's physical blocks ("PagedAttention por
+ * dentro...", section "El pool de bloques": one pool shared by every session).  A
+ * block is free (count 0) or allocated (count >= 1).  Every call keeps free +
+ * allocated == pool size; a call that fails changes nothing.  Thread-safe (one lock
+ * per pool).  The pool's host memory is allocated by pkv_pool_create and freed by
+ * pkv_pool_destroy; nothing on the device.
+ *   pkv_pool_alloc   : n free blocks, count 1 each, into ids_out (all or nothing;
+ *                      PKV_ERR_POOL_EXHAUSTED when fewer are free)
+ *   pkv_pool_share   : one more reference to each (prefix caching, forked branches)
+ *   pkv_pool_release : one reference less to each (an ID may repeat); a block whose
+ *                      count reaches 0 is free again
+ *   pkv_pool_cow     : before writing into block id: returns 0 with *id_out = id when
+ *                      the caller holds the only reference, else 1 with *id_out a
+ *                      fresh block (count 1) whose contents the caller copies with
+ *                      paged_kv_copy_blocks, id losing the caller's reference
+ * Errors: PKV_ERR_BLOCK_STATE for an ID out of range or not allocated (or released
+ * more times than referenced), PKV_ERR_NULL, PKV_ERR_SHAPE for n < 0.
+ */
+typedef struct pkv_block_pool pkv_block_pool;
+pkv_block_pool* pkv_pool_create(int32_t num_blocks); /* NULL if num_blocks <= 0 or no memory */
+void pkv_pool_destroy(pkv_block_pool* pool);
+int pkv_pool_alloc(pkv_block_pool* pool, int32_t n, int32_t* ids_out);
+int pkv_pool_share(pkv_block_pool* pool, const int32_t* ids, int32_t n);
+int pkv_pool_release(pkv_block_pool* pool, const int32_t* ids, int32_t n);
+int pkv_pool_cow(pkv_block_pool* pool, int32_t id, int32_t* id_out);
+int32_t pkv_pool_free_count(pkv_block_pool* pool);              /* >= 0, or an error */
+int32_t pkv_pool_refcount(pkv_block_pool* pool, int32_t id);    /* >= 0, or an error */
 
 /* Static description of a status code. */
 const char* pkv_status_string(int status);

@@ -14,6 +14,8 @@
  *                           exact two-pass softmax in fp64.
  *   oracle_decode_window -- the same over a sliding window of the last tokens plus
  *                           the first (sink) tokens.
+ *   oracle_copy_blocks   -- copy-on-write copy of whole physical blocks.
+ *   oracle_swap_blocks   -- blocks to / from a contiguous (host) buffer.
  *   oracle_kv_bytes      -- the pages' KV-memory closed form.
  *   codecs               -- bf16 / fp16 / OCP e4m3fn decoders, e4m3fn encoder.
  *
@@ -209,6 +211,64 @@ int oracle_kv_write(const int64_t* slot_mapping, int64_t num_tokens, const void*
         memcpy((char*)v_cache + dst * cb, (const char*)(MUT(5) ? k : v) + src * sb,
                (size_t)d_h * cb);
       }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------ block copies, swap -- */
+
+/* Copy-on-write: for each pair i, the whole physical block src[i] (every KV head, K
+ * and V) is copied to block dst[i], so that the sequence about to write into a shared
+ * block gets a private copy first ("PagedAttention por dentro...", section
+ * "Copy-on-write para sampling paralelo": only the last affected block is copied when
+ * a branch diverges; "La despensa por casilleros", section "Prefix caching...": the
+ * block manager copies the block for that branch and only then writes).  A pair with
+ * a negative ID is skipped.  All sources are read before any destination is written.
+ * block_bytes = H_kv * B * d_h * element bytes.
+ */
+int oracle_copy_blocks(const int32_t* src, const int32_t* dst, int64_t num_pairs, void* k_cache,
+                       void* v_cache, int64_t num_blocks, int64_t block_bytes) {
+  if (num_pairs <= 0) return 0;
+  char* tmp = (char*)malloc((size_t)(2 * num_pairs * block_bytes));
+  if (!tmp) return -7;
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    if (src[i] < 0 || dst[i] < 0) continue;
+    if (src[i] >= num_blocks || dst[i] >= num_blocks) { free(tmp); return -5; }
+    memcpy(tmp + (2 * i) * block_bytes, (char*)k_cache + src[i] * block_bytes, (size_t)block_bytes);
+    memcpy(tmp + (2 * i + 1) * block_bytes, (char*)(MUT(11) ? k_cache : v_cache) + src[i] * block_bytes,
+           (size_t)block_bytes);
+  }
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    if (src[i] < 0 || dst[i] < 0) continue;
+    memcpy((char*)k_cache + dst[i] * block_bytes, tmp + (2 * i) * block_bytes, (size_t)block_bytes);
+    memcpy((char*)v_cache + dst[i] * block_bytes, tmp + (2 * i + 1) * block_bytes, (size_t)block_bytes);
+  }
+  free(tmp);
+  return 0;
+}
+
+/* Swap out: block ids[i] of each cache goes to row i of a contiguous buffer
+ * ([num][block_bytes] for K, the same for V); swap in: row i comes back into block
+ * ids[i] ("PagedAttention por dentro...", section "Estrategia 2: swap": the evicted
+ * session's blocks move to CPU RAM and come back to VRAM when it is resumed).  A
+ * negative ID skips its row.  direction 0 = out (cache -> buffer), 1 = in.
+ */
+int oracle_swap_blocks(const int32_t* ids, int64_t num, void* k_cache, void* v_cache,
+                       void* k_buf, void* v_buf, int64_t num_blocks, int64_t block_bytes, int direction) {
+  for (int64_t i = 0; i < num; ++i) {
+    if (ids[i] < 0) continue;
+    if (ids[i] >= num_blocks) return -5;
+    char* kc = (char*)k_cache + ids[i] * block_bytes;
+    char* vc = (char*)v_cache + ids[i] * block_bytes;
+    char* kb = (char*)k_buf + i * block_bytes;
+    char* vb = (char*)v_buf + i * block_bytes;
+    if (direction == 0) {
+      memcpy(kb, kc, (size_t)block_bytes);
+      memcpy(vb, vc, (size_t)block_bytes);
+    } else {
+      memcpy(kc, kb, (size_t)block_bytes);
+      memcpy(vc, vb, (size_t)block_bytes);
     }
   }
   return 0;

@@ -75,6 +75,13 @@ class Oracle:
                                              ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, _f64p,
                                              ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+        lib.oracle_copy_blocks.restype = ctypes.c_int
+        lib.oracle_copy_blocks.argtypes = [_i32p, _i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int64]
+        lib.oracle_swap_blocks.restype = ctypes.c_int
+        lib.oracle_swap_blocks.argtypes = [_i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int]
         lib.oracle_mutation.restype = ctypes.c_int
         self.mutation = lib.oracle_mutation()
 
@@ -124,6 +131,40 @@ class Oracle:
                                       nb, bs, hkv, d, CODES[cache_dtype], k_scale, v_scale)
         if rc:
             raise ValueError(f"oracle_kv_write failed: {rc}")
+
+    def copy_blocks(self, src, dst, k_cache, v_cache) -> None:
+        """Copy-on-write: block src[i] -> block dst[i] in both caches (in place)."""
+        src = np.ascontiguousarray(src, dtype=np.int32)
+        dst = np.ascontiguousarray(dst, dtype=np.int32)
+        assert src.shape == dst.shape and k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+        nb = k_cache.shape[0]
+        rc = self.lib.oracle_copy_blocks(src, dst, src.size, k_cache.ctypes.data, v_cache.ctypes.data,
+                                         nb, k_cache.nbytes // nb)
+        if rc:
+            raise ValueError(f"oracle_copy_blocks failed: {rc}")
+
+    def swap_out(self, ids, k_cache, v_cache):
+        """Blocks ids[i] of each cache as rows of new contiguous arrays (K, V)."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        nb = k_cache.shape[0]
+        kb = np.zeros((ids.size,) + k_cache.shape[1:], dtype=k_cache.dtype)
+        vb = np.zeros_like(kb)
+        rc = self.lib.oracle_swap_blocks(ids, ids.size, k_cache.ctypes.data, v_cache.ctypes.data,
+                                         kb.ctypes.data, vb.ctypes.data, nb, k_cache.nbytes // nb, 0)
+        if rc:
+            raise ValueError(f"oracle_swap_blocks failed: {rc}")
+        return kb, vb
+
+    def swap_in(self, ids, k_buf, v_buf, k_cache, v_cache) -> None:
+        """Rows i of the contiguous arrays back into blocks ids[i] (in place)."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        k_buf = np.ascontiguousarray(k_buf)
+        v_buf = np.ascontiguousarray(v_buf)
+        nb = k_cache.shape[0]
+        rc = self.lib.oracle_swap_blocks(ids, ids.size, k_cache.ctypes.data, v_cache.ctypes.data,
+                                         k_buf.ctypes.data, v_buf.ctypes.data, nb, k_cache.nbytes // nb, 1)
+        if rc:
+            raise ValueError(f"oracle_swap_blocks failed: {rc}")
 
     def decode(self, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, context_lens,
                scale, k_scale=1.0, v_scale=1.0, pairs=None, threads=1, count_bytes=False,

@@ -20,11 +20,15 @@ _TORCH_CODES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
 _NAME_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8_E4M3}
 
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHAPE",
-          -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH"}
+          -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH",
+          -7: "PKV_ERR_POOL_EXHAUSTED", -8: "PKV_ERR_BLOCK_STATE"}
 
 EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_schedule",
             "paged_attention_workspace_size", "paged_attention_decode", "paged_attention_decode_window",
             "paged_attention_shared_prefix_workspace_size", "paged_attention_decode_shared_prefix",
+            "paged_kv_copy_blocks", "paged_kv_swap_out", "paged_kv_swap_in",
+            "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_alloc", "pkv_pool_share", "pkv_pool_release",
+            "pkv_pool_cow", "pkv_pool_free_count", "pkv_pool_refcount",
             "pkv_status_string", "pkv_abi_version"]
 SCHEDULES = {0: "single-pass", 1: "fixed-partitions", 2: "balanced"}
 
@@ -86,6 +90,29 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
                                                          vp, i32, i32, vp, i32, f32, vp, ctypes.c_int,
                                                          vp, ctypes.c_size_t, vp]
     lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
+    lib.paged_kv_copy_blocks.argtypes = [vp, vp, i32, vp, vp, ctypes.POINTER(CacheDesc), vp]
+    lib.paged_kv_copy_blocks.restype = ctypes.c_int
+    lib.paged_kv_swap_out.argtypes = [vp, i32, vp, vp, ctypes.POINTER(CacheDesc), vp, vp, vp]
+    lib.paged_kv_swap_out.restype = ctypes.c_int
+    lib.paged_kv_swap_in.argtypes = [vp, i32, vp, vp, vp, vp, ctypes.POINTER(CacheDesc), vp]
+    lib.paged_kv_swap_in.restype = ctypes.c_int
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.pkv_pool_create.argtypes = [i32]
+    lib.pkv_pool_create.restype = vp
+    lib.pkv_pool_destroy.argtypes = [vp]
+    lib.pkv_pool_destroy.restype = None
+    lib.pkv_pool_alloc.argtypes = [vp, i32, i32p]
+    lib.pkv_pool_alloc.restype = ctypes.c_int
+    lib.pkv_pool_share.argtypes = [vp, i32p, i32]
+    lib.pkv_pool_share.restype = ctypes.c_int
+    lib.pkv_pool_release.argtypes = [vp, i32p, i32]
+    lib.pkv_pool_release.restype = ctypes.c_int
+    lib.pkv_pool_cow.argtypes = [vp, i32, i32p]
+    lib.pkv_pool_cow.restype = ctypes.c_int
+    lib.pkv_pool_free_count.argtypes = [vp]
+    lib.pkv_pool_free_count.restype = ctypes.c_int32
+    lib.pkv_pool_refcount.argtypes = [vp, i32]
+    lib.pkv_pool_refcount.restype = ctypes.c_int32
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -174,6 +201,96 @@ def paged_kv_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check("paged_kv_write",
            lib.paged_kv_write(_ptr(slot_mapping), slot_mapping.numel(), _ptr(k), _ptr(v), src,
                               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def paged_kv_copy_blocks(src_ids: torch.Tensor, dst_ids: torch.Tensor, k_cache: torch.Tensor,
+                         v_cache: torch.Tensor, kv_dtype=None, stream=None) -> None:
+    """Copy-on-write: block src_ids[i] -> dst_ids[i] in both caches (int32 device IDs)."""
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype)
+    assert src_ids.dtype == torch.int32 and dst_ids.dtype == torch.int32 and src_ids.numel() == dst_ids.numel()
+    _check("paged_kv_copy_blocks",
+           lib.paged_kv_copy_blocks(_ptr(src_ids), _ptr(dst_ids), src_ids.numel(), _ptr(k_cache),
+                                    _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def paged_kv_swap_out(ids: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      k_buf: torch.Tensor, v_buf: torch.Tensor, kv_dtype=None, stream=None) -> None:
+    """Blocks ids[i] of each cache -> row i of the device buffers ([n][block elements])."""
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype)
+    assert ids.dtype == torch.int32
+    _check("paged_kv_swap_out",
+           lib.paged_kv_swap_out(_ptr(ids), ids.numel(), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                                 _ptr(k_buf), _ptr(v_buf), _stream(stream)))
+
+
+def paged_kv_swap_in(ids: torch.Tensor, k_buf: torch.Tensor, v_buf: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, kv_dtype=None, stream=None) -> None:
+    """Row i of the device buffers -> blocks ids[i] of each cache."""
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype)
+    assert ids.dtype == torch.int32
+    _check("paged_kv_swap_in",
+           lib.paged_kv_swap_in(_ptr(ids), ids.numel(), _ptr(k_buf), _ptr(v_buf), _ptr(k_cache),
+                                _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+class BlockPoolHandle:
+    """The library's host-side refcounted block pool (pkv_pool_*), one per cache."""
+
+    def __init__(self, num_blocks: int):
+        self.lib = load_library()
+        self.h = self.lib.pkv_pool_create(int(num_blocks))
+        if not self.h:
+            raise PagedKVError("pkv_pool_create", -3, "could not create the pool")
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            self.lib.pkv_pool_destroy(self.h)
+            self.h = None
+
+    @staticmethod
+    def _ids(ids):
+        import numpy as np
+        a = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def alloc(self, n: int):
+        import numpy as np
+        out = np.empty(int(n), dtype=np.int32)
+        _check("pkv_pool_alloc", self.lib.pkv_pool_alloc(self.h, int(n),
+                                                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return out
+
+    def share(self, ids) -> None:
+        a, p = self._ids(ids)
+        _check("pkv_pool_share", self.lib.pkv_pool_share(self.h, p, a.size))
+
+    def release(self, ids) -> None:
+        a, p = self._ids(ids)
+        _check("pkv_pool_release", self.lib.pkv_pool_release(self.h, p, a.size))
+
+    def cow(self, block: int):
+        """(block to write into, whether its contents must be copied from `block` first)."""
+        out = ctypes.c_int32(-1)
+        rc = self.lib.pkv_pool_cow(self.h, int(block), ctypes.byref(out))
+        if rc < 0:
+            _check("pkv_pool_cow", rc)
+        return int(out.value), rc == 1
+
+    def free_count(self) -> int:
+        n = self.lib.pkv_pool_free_count(self.h)
+        if n < 0:
+            _check("pkv_pool_free_count", n)
+        return int(n)
+
+    def refcount(self, block: int) -> int:
+        n = self.lib.pkv_pool_refcount(self.h, int(block))
+        if n < 0:
+            _check("pkv_pool_refcount", n)
+        return int(n)
 
 
 def paged_attention_workspace_size(desc: CacheDesc, q_dtype, num_seqs: int, num_q_heads: int,

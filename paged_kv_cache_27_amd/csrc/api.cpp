@@ -45,6 +45,12 @@ int check_decode_shape(const pkv_cache_desc* cache, int q_dtype, int out_dtype, 
   return PKV_OK;
 }
 
+// Bytes of one physical block of one cache: H_kv * B * d_h elements.
+int64_t block_bytes(const pkv_cache_desc* c) {
+  const int64_t eb = c->dtype == PKV_F32 ? 4 : (c->dtype == PKV_FP8_E4M3 ? 1 : 2);
+  return (int64_t)c->num_kv_heads * c->block_size * c->head_dim * eb;
+}
+
 // How a decode call is scheduled.
 enum Mode { kSingle = 0, kFixed = 1, kBalanced = 2 };
 
@@ -140,7 +146,7 @@ int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 4; }
+int32_t pkv_abi_version(void) { return 5; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -151,6 +157,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_HEADS: return "num_q_heads is not a multiple of num_kv_heads";
     case PKV_ERR_WORKSPACE: return "workspace too small or bad partition size";
     case PKV_ERR_LAUNCH: return "HIP launch error";
+    case PKV_ERR_POOL_EXHAUSTED: return "block pool: not enough free blocks";
+    case PKV_ERR_BLOCK_STATE: return "block pool: block ID out of range or not allocated";
     default: return "unknown status";
   }
 }
@@ -193,6 +201,47 @@ int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* 
   a.k_scale = cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f;
   a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
   hipError_t e = pkv::launch_kv_write(a, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_kv_copy_blocks(const int32_t* src_ids, const int32_t* dst_ids, int32_t num_pairs,
+                         void* k_cache, void* v_cache, const pkv_cache_desc* cache, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_ids || !dst_ids || !k_cache || !v_cache) return PKV_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
+  hipError_t e = pkv::launch_move_blocks(k_cache, v_cache, src_ids, k_cache, v_cache, dst_ids, num_pairs,
+                                         block_bytes(cache), stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_kv_swap_out(const int32_t* ids, int32_t num, const void* k_cache, const void* v_cache,
+                      const pkv_cache_desc* cache, void* k_buf, void* v_buf, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num < 0) return PKV_ERR_SHAPE;
+  if (num == 0) return PKV_OK;
+  if (!ids || !k_cache || !v_cache || !k_buf || !v_buf) return PKV_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
+    return PKV_ERR_SHAPE;
+  hipError_t e = pkv::launch_move_blocks(k_cache, v_cache, ids, k_buf, v_buf, nullptr, num,
+                                         block_bytes(cache), stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const void* v_buf,
+                     void* k_cache, void* v_cache, const pkv_cache_desc* cache, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num < 0) return PKV_ERR_SHAPE;
+  if (num == 0) return PKV_OK;
+  if (!ids || !k_cache || !v_cache || !k_buf || !v_buf) return PKV_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
+    return PKV_ERR_SHAPE;
+  hipError_t e = pkv::launch_move_blocks(k_buf, v_buf, nullptr, k_cache, v_cache, ids, num,
+                                         block_bytes(cache), stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -73,6 +73,13 @@ struct PrefixArgs {
 constexpr int kPrefixRows = 64;  // query rows per workgroup of the prefix kernel
 hipError_t launch_prefix(const PrefixArgs& a, int num_groups, hipStream_t stream);
 
+// Whole-block moves (copy-on-write, swap): pair i moves block src_ids[i] (row i when
+// src_ids is null) of each of the K and V sources to block dst_ids[i] (row i when
+// dst_ids is null) of the destinations; a negative ID skips the pair.
+hipError_t launch_move_blocks(const void* k_src, const void* v_src, const int32_t* src_ids, void* k_dst,
+                              void* v_dst, const int32_t* dst_ids, int32_t num, int64_t block_bytes,
+                              hipStream_t stream);
+
 hipError_t launch_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t n,
                                const int32_t* block_tables, int32_t max_blocks,
                                int32_t block_size, int64_t* slots, hipStream_t stream);

@@ -284,9 +284,43 @@ def pin_window_freed_blocks_unread(orc):
         assert np.isfinite(got).all() and np.array_equal(got, ref), (W, S)
 
 
+def _random_cache(rng, shape=(12, 2, 16, 64), dtype=np.uint16):
+    return rng.integers(0, 2**16, size=shape, dtype=np.int64).astype(dtype)
+
+
+def pin_copy_blocks(orc):
+    """Copy-on-write copies == numpy's gather-then-assign of whole blocks, K and V each;
+    pairs with a negative ID change nothing."""
+    rng = np.random.default_rng(11)
+    kc, vc = _random_cache(rng), _random_cache(rng)
+    src = np.array([3, 7, 7, -1, 0], np.int32)
+    dst = np.array([9, 1, 4, 5, 11], np.int32)
+    k_ref, v_ref = kc.copy(), vc.copy()
+    keep = (src >= 0) & (dst >= 0)
+    k_ref[dst[keep]] = kc[src[keep]]
+    v_ref[dst[keep]] = vc[src[keep]]
+    orc.copy_blocks(src, dst, kc, vc)
+    assert np.array_equal(kc, k_ref) and np.array_equal(vc, v_ref)
+
+
+def pin_swap_round_trip(orc):
+    """Swap out returns exactly the listed blocks; swapping them back into other blocks
+    equals copying them there."""
+    rng = np.random.default_rng(12)
+    kc, vc = _random_cache(rng), _random_cache(rng)
+    ids = np.array([2, 5, 8], np.int32)
+    kb, vb = orc.swap_out(ids, kc, vc)
+    assert np.array_equal(kb, kc[ids]) and np.array_equal(vb, vc[ids])
+    k2, v2 = kc.copy(), vc.copy()
+    orc.swap_in(np.array([10, 0, 3], np.int32), kb, vb, k2, v2)
+    k3, v3 = kc.copy(), vc.copy()
+    orc.copy_blocks(ids, np.array([10, 0, 3], np.int32), k3, v3)
+    assert np.array_equal(k2, k3) and np.array_equal(v2, v3)
+
+
 ALL_PINS = [pin_kv_bytes_golden, pin_block_addressing_golden, pin_dense_equivalence,
             pin_ctx1_returns_new_value, pin_equal_keys_mean_value, pin_zero_query_mean_value,
             pin_permutation_invariance, pin_gqa_head_mapping, pin_bytes_touched,
             pin_write_placement, pin_fp8_codec, pin_fp8_saturation, pin_half_codecs,
             pin_window_dense, pin_window_one_is_last_value, pin_window_covering_is_full,
-            pin_window_freed_blocks_unread]
+            pin_window_freed_blocks_unread, pin_copy_blocks, pin_swap_round_trip]

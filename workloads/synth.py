@@ -61,6 +61,10 @@ class DecodeConfig:
     # "prefix" contexts: the sequences form this many contiguous groups (group k is
     # sequences [N k / groups, N (k+1) / groups)); each group shares its own prefix blocks.
     prefix_groups: int = 1
+    # decode over a sliding window: the last `window` tokens of each context plus its
+    # first `sinks` (0 = the whole context)
+    window: int = 0
+    sinks: int = 0
 
     @property
     def group(self) -> int:
@@ -82,6 +86,11 @@ PREFIX = DecodeConfig("prefix-sharing-bf16-256seq-b32", 256, 32, 8, 128, 32, "bf
 LONGCTX = DecodeConfig("long-context-bf16-8seq-32k", 8, 32, 8, 128, 16, "bf16", "bf16",
                        "bf16", "bf16", "const", (32768,), partition_size=512, seed=1005)
 CONFIGS = [TINY, LLAMA8B, R70B_FP8, PREFIX, LONGCTX]
+# Beyond the five: the long-context layer decoded over a Mistral-style window of the last
+# 4096 tokens plus 4 attention-sink tokens (the blocks in between freed).
+LONGCTX_WINDOW = LONGCTX.replace(name="long-context-window4096-sinks4-bf16-8seq-32k", window=4096,
+                                 sinks=4, partition_size=0)
+EXTRA_CONFIGS = [LONGCTX_WINDOW]
 
 
 def context_lengths(cfg: DecodeConfig, rng: np.random.Generator) -> np.ndarray:
