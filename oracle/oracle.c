@@ -14,6 +14,8 @@
  *                           exact two-pass softmax in fp64.
  *   oracle_decode_window -- the same over a sliding window of the last tokens plus
  *                           the first (sink) tokens.
+ *   oracle_prefill       -- chunked prefill: many causal query tokens per sequence
+ *                           over the same paged cache.
  *   oracle_copy_blocks   -- copy-on-write copy of whole physical blocks.
  *   oracle_swap_blocks   -- blocks to / from a contiguous (host) buffer.
  *   oracle_kv_bytes      -- the pages' KV-memory closed form.
@@ -374,6 +376,77 @@ int oracle_decode_window(const void* q, int q_dtype, int32_t num_seqs, int32_t n
   }
   (void)num_blocks;
   if (bytes_read) *bytes_read += total_bytes;
+  return status;
+}
+
+/* Chunked prefill over the paged cache: sequence s brings n_s = cu_q[s+1] - cu_q[s]
+ * query tokens, rows cu_q[s] .. cu_q[s+1]-1 of q / out ([rows][H_q][d_h]); they are the
+ * last n_s tokens of its context (their K/V already written), so query i sits at
+ * position p = ctx[s] - n_s + i and attends, causally, to tokens 0 .. p of the paged
+ * cache:
+ *   out[row][h][:] = softmax_{t <= p}(scale * q[row][h] . K_t) @ V_t
+ * ("PagedAttention por dentro...", section "Chunked prefill integrado con paged KV": the
+ * prompt is cut into chunks that run in the same step as decodes, over the same paged
+ * KV cache; "Componentes Internos de Servicio de vLLM", section "Chunked prefill
+ * protege la cola del TTFT": fixed-size chunks, 512 tokens by default).  A decode is
+ * the one-token chunk.  Exact two-pass softmax in fp64, as oracle_decode.
+ */
+int oracle_prefill(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                   const int32_t* cu_q, const void* k_cache, const void* v_cache, int cache_dtype,
+                   float k_scale, float v_scale, int32_t block_size, int32_t H_kv, int32_t d_h,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, float scale, double* out, int num_threads) {
+  if (H_kv <= 0 || num_q_heads % H_kv) return -4;
+  if (!elem_bytes(q_dtype) || !elem_bytes(cache_dtype)) return -2;
+  const int32_t G = num_q_heads / H_kv;
+  const int64_t rows = cu_q[num_seqs];
+  int status = 0;
+  double kscale = cache_dtype == O_FP8 ? (double)k_scale : 1.0;
+  double vscale = cache_dtype == O_FP8 ? (double)v_scale : 1.0;
+#ifdef _OPENMP
+  if (num_threads <= 0) num_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads)
+#endif
+  for (int64_t r = 0; r < rows * num_q_heads; ++r) {
+    const int64_t row = r / num_q_heads;
+    const int32_t h = (int32_t)(r % num_q_heads);
+    int32_t s = 0;
+    while (cu_q[s + 1] <= row) ++s;
+    const int32_t n = cu_q[s + 1] - cu_q[s];
+    const int32_t i = (int32_t)(row - cu_q[s]);
+    const int32_t pos = context_lens[s] - n + i;
+    const int32_t g = h / G;
+    double* o = out + r * d_h;
+    for (int32_t d = 0; d < d_h; ++d) o[d] = 0.0;
+    const int32_t na = MUT(12) ? pos : pos + 1; /* tokens 0 .. pos */
+    if (na <= 0) continue;
+    double* z = (double*)malloc(sizeof(double) * (size_t)na);
+    if (!z) { status = -7; continue; }
+    const int64_t q_base = r * d_h;
+    for (int32_t t = 0; t < na; ++t) {
+      int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+      int64_t krow = ((phys * H_kv + g) * block_size + t % block_size) * d_h;
+      double acc = 0.0;
+      for (int32_t d = 0; d < d_h; ++d)
+        acc += load_f64(q, q_base + d, q_dtype) * (load_f64(k_cache, krow + d, cache_dtype) * kscale);
+      z[t] = (double)scale * acc;
+    }
+    double m = z[0];
+    for (int32_t t = 1; t < na; ++t)
+      if (z[t] > m) m = z[t];
+    double wsum = 0.0;
+    for (int32_t t = 0; t < na; ++t) {
+      z[t] = exp(z[t] - m);
+      wsum += z[t];
+    }
+    for (int32_t t = 0; t < na; ++t) {
+      int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+      int64_t vrow = ((phys * H_kv + g) * block_size + t % block_size) * d_h;
+      for (int32_t d = 0; d < d_h; ++d) o[d] += z[t] * (load_f64(v_cache, vrow + d, cache_dtype) * vscale);
+    }
+    for (int32_t d = 0; d < d_h; ++d) o[d] /= wsum;
+    free(z);
+  }
   return status;
 }
 

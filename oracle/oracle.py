@@ -75,6 +75,11 @@ class Oracle:
                                              ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, _f64p,
                                              ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+        lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_prefill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       _i32p, ctypes.c_int32, _i32p, ctypes.c_float, _f64p, ctypes.c_int]
         lib.oracle_copy_blocks.restype = ctypes.c_int
         lib.oracle_copy_blocks.argtypes = [_i32p, _i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_int64]
@@ -131,6 +136,26 @@ class Oracle:
                                       nb, bs, hkv, d, CODES[cache_dtype], k_scale, v_scale)
         if rc:
             raise ValueError(f"oracle_kv_write failed: {rc}")
+
+    def prefill(self, q, q_dtype, cu_q, k_cache, v_cache, cache_dtype, block_tables, context_lens,
+                scale, k_scale=1.0, v_scale=1.0, threads=1):
+        """Causal attention of each sequence's last cu_q[s+1]-cu_q[s] tokens (rows of q,
+        [rows][H_q][d_h]) over its paged context.  Returns [rows][H_q][d_h] fp64."""
+        q = np.ascontiguousarray(q)
+        rows, hq, d = q.shape
+        nb, hkv, bs, d2 = k_cache.shape
+        assert d == d2
+        cu = np.ascontiguousarray(cu_q, dtype=np.int32)
+        assert cu[-1] == rows
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        out = np.zeros((rows, hq, d), dtype=np.float64)
+        rc = self.lib.oracle_prefill(q.ctypes.data, CODES[q_dtype], cu.size - 1, hq, cu, k_cache.ctypes.data,
+                                     v_cache.ctypes.data, CODES[cache_dtype], k_scale, v_scale, bs, hkv, d,
+                                     bt, bt.shape[1], cl, scale, out, threads)
+        if rc:
+            raise ValueError(f"oracle_prefill failed: {rc}")
+        return out
 
     def copy_blocks(self, src, dst, k_cache, v_cache) -> None:
         """Copy-on-write: block src[i] -> block dst[i] in both caches (in place)."""

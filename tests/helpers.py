@@ -70,6 +70,28 @@ def free_blocks_outside_window(w, window: int, sinks: int) -> np.ndarray:
     return bt
 
 
+def dense_causal(w, s: int, q_row: np.ndarray, pos: int) -> np.ndarray:
+    """softmax(q K^T * scale) V over tokens 0 .. pos of sequence s's contiguous K/V for one
+    query row [H_q][D] in the query dtype (fp64, numpy), per query head."""
+    c = w.cfg
+    k, v = w.logical_kv(s)
+    k, v = k[:pos + 1], v[:pos + 1]
+    if c.kv_dtype == "fp8":
+        kf = storage_to_f64(torch_fp8_quantise(k, c.src_dtype, w.k_scale), "fp8") * w.k_scale
+        vf = storage_to_f64(torch_fp8_quantise(v, c.src_dtype, w.v_scale), "fp8") * w.v_scale
+    else:
+        kf = storage_to_f64(k, c.kv_dtype)
+        vf = storage_to_f64(v, c.kv_dtype)
+    q = storage_to_f64(q_row, c.q_dtype)
+    G = c.group
+    out = np.empty((c.num_q_heads, c.head_dim))
+    for h in range(c.num_q_heads):
+        z = (kf[:, h // G, :] @ q[h]) * float(w.scale)
+        p = np.exp(z - z.max())
+        out[h] = (p @ vf[:, h // G, :]) / p.sum()
+    return out
+
+
 def dense_reference(w, s: int, window: int = 0, sinks: int = 0) -> np.ndarray:
     """softmax(q K^T * scale) V per query head on sequence s's contiguous K/V (fp64, numpy),
     over the attended rows (all of them unless a window is given).

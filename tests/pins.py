@@ -14,8 +14,9 @@ from pathlib import Path
 import numpy as np
 import torch
 
-from helpers import dense_reference, free_blocks_outside_window, oracle_step, storage_to_f64
-from workloads import LLAMA8B, LONGCTX, PREFIX, R70B_FP8, TINY, make_workload
+from helpers import (dense_causal, dense_reference, free_blocks_outside_window, oracle_step,
+                     storage_to_f64)
+from workloads import LLAMA8B, LONGCTX, PREFIX, R70B_FP8, TINY, make_workload, prefill_queries
 
 GOLDEN = Path(__file__).resolve().parent / "golden"
 
@@ -318,9 +319,58 @@ def pin_swap_round_trip(orc):
     assert np.array_equal(k2, k3) and np.array_equal(v2, v3)
 
 
+def _prefill(orc, w, kc, vc, q, cu, context_lens=None):
+    c = w.cfg
+    return orc.prefill(q, c.q_dtype, cu, kc, vc, c.kv_dtype, w.block_tables,
+                       w.context_lens if context_lens is None else context_lens, w.scale, w.k_scale,
+                       w.v_scale)
+
+
+def pin_prefill_one_token_is_decode(orc):
+    """A chunk of one token per sequence is a decode step: bit-identical outputs."""
+    for name in ("llama8b", "r70b", "tiny"):
+        w = make_workload(SMALL[name])
+        kc, vc, _, dec = oracle_step(orc, w)
+        cu = np.arange(w.cfg.num_seqs + 1, dtype=np.int32)
+        assert np.array_equal(_prefill(orc, w, kc, vc, w.q, cu), dec), name
+
+
+def pin_prefill_dense_causal(orc):
+    """Each query token of a chunk == dense softmax over the contiguous K/V rows up to and
+    including its own position (numpy, fp64), <= 1e-12."""
+    for name, lens in (("llama8b", (9, 40, 1)), ("r70b", (16, 3, 33)), ("mqa", (20, 60))):
+        w = make_workload(SMALL[name].replace(num_seqs=len(lens), ctx_kind="fixed",
+                                              ctx_params=tuple(sorted(l + 30 for l in lens))))
+        kc, vc, _, _ = oracle_step(orc, w)
+        n = np.minimum(np.array(lens), w.context_lens)
+        q, cu = prefill_queries(w, n)
+        out = _prefill(orc, w, kc, vc, q, cu)
+        c = w.cfg
+        for s in range(c.num_seqs):
+            for i in range(int(n[s])):
+                pos = int(w.context_lens[s]) - int(n[s]) + i
+                ref = dense_causal(w, s, q[cu[s] + i], pos)
+                err = np.abs(out[cu[s] + i] - ref).max()
+                assert err <= 1e-12, (name, s, i, err)
+
+
+def pin_prefill_chunking_invariance(orc):
+    """The outputs of a prompt's query tokens do not depend on how it is cut into chunks:
+    one 40-token chunk == the same queries as a 25-token then a 15-token chunk (context
+    grown between them), bit for bit."""
+    w = make_workload(SMALL["llama8b"].replace(num_seqs=1, ctx_kind="fixed", ctx_params=(70,)))
+    kc, vc, _, _ = oracle_step(orc, w)
+    q, cu = prefill_queries(w, [40])
+    whole = _prefill(orc, w, kc, vc, q, cu)
+    first = _prefill(orc, w, kc, vc, q[:25], np.array([0, 25], np.int32), np.array([55], np.int32))
+    second = _prefill(orc, w, kc, vc, q[25:], np.array([0, 15], np.int32))
+    assert np.array_equal(np.concatenate([first, second]), whole)
+
+
 ALL_PINS = [pin_kv_bytes_golden, pin_block_addressing_golden, pin_dense_equivalence,
             pin_ctx1_returns_new_value, pin_equal_keys_mean_value, pin_zero_query_mean_value,
             pin_permutation_invariance, pin_gqa_head_mapping, pin_bytes_touched,
             pin_write_placement, pin_fp8_codec, pin_fp8_saturation, pin_half_codecs,
             pin_window_dense, pin_window_one_is_last_value, pin_window_covering_is_full,
-            pin_window_freed_blocks_unread, pin_copy_blocks, pin_swap_round_trip]
+            pin_window_freed_blocks_unread, pin_copy_blocks, pin_swap_round_trip,
+            pin_prefill_one_token_is_decode, pin_prefill_dense_causal, pin_prefill_chunking_invariance]

@@ -6,7 +6,7 @@ Mutations (see the MUT() sites in oracle/oracle.c):
  3 block index and offset swapped         7 fp8 encode truncates instead of RNE
  4 softmax scale dropped                  8 bf16 decoded with the wrong shift
  9 window start off by one                10 sink tokens left out of a window
-11 copy-on-write copies K into the V cache
+11 copy-on-write copies K into the V cache     12 prefill query misses its own token
 """
 import pytest
 
@@ -17,7 +17,7 @@ EXPECTED = {
     1: "pin_gqa_head_mapping", 2: "pin_dense_equivalence", 3: "pin_block_addressing_golden",
     4: "pin_dense_equivalence", 5: "pin_write_placement", 6: "pin_ctx1_returns_new_value",
     7: "pin_fp8_codec", 8: "pin_half_codecs", 9: "pin_window_one_is_last_value",
-    10: "pin_window_dense", 11: "pin_copy_blocks",
+    10: "pin_window_dense", 11: "pin_copy_blocks", 12: "pin_prefill_one_token_is_decode",
 }
 
 

@@ -352,6 +352,21 @@ def cache_shape(w: Workload) -> tuple:
     return (w.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
 
 
+def prefill_queries(w: Workload, chunk_lens, seed: int = 77):
+    """Query rows of a chunked-prefill step over workload w: sequence s brings
+    chunk_lens[s] query tokens (the last ones of its context, <= its length), drawn
+    ~N(0,1) in the query dtype like decode queries.  Returns (q [rows][H_q][d_h],
+    cu_q [N + 1] int32)."""
+    c = w.cfg
+    n = np.asarray(chunk_lens, dtype=np.int32)
+    assert n.shape == (c.num_seqs,) and (n >= 0).all() and (n <= w.context_lens).all()
+    cu = np.zeros(c.num_seqs + 1, np.int32)
+    cu[1:] = np.cumsum(n)
+    gen = torch.Generator().manual_seed(seed)
+    q = _random_values(gen, (int(cu[-1]), c.num_q_heads, c.head_dim), c.q_dtype)
+    return q, cu
+
+
 def poisoned_cache(w: Workload) -> np.ndarray:
     """A cache array of the workload's KV dtype with every element set to NaN."""
     dt = w.cfg.kv_dtype
