@@ -248,6 +248,31 @@ int paged_attention_decode_shared_prefix(
     int32_t max_prefix_len, float scale, void* out, pkv_dtype out_dtype, void* workspace,
     size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Chunked prefill over the paged cache: each sequence brings a chunk of new query tokens,
+ * the last n_s of its context (their K/V already written with paged_kv_write), and query i
+ * of the chunk, at position context_lens[s] - n_s + i, attends causally to tokens 0 ..
+ * that position ("PagedAttention por dentro...", section "Chunked prefill integrado con
+ * paged KV": prompts cut into chunks that run in the same step as decodes, over the same
+ * paged KV cache; "Componentes Internos de Servicio de vLLM", section "Chunked prefill
+ * protege la cola del TTFT": 512-token chunks by default).  A one-token chunk is a decode.
+ *   q            : [rows][num_q_heads][head_dim] of q_dtype, rows = cu_q[num_seqs]
+ *   cu_q         : int32 [num_seqs + 1] device, ascending from 0: the query rows of
+ *                  sequence s are cu_q[s] .. cu_q[s+1]-1 (n_s = cu_q[s+1] - cu_q[s])
+ *   max_q_len    : host-side upper bound of n_s (sizes the grid), <= max_context_len
+ *   context_lens : int32 [num_seqs], counting the chunk (n_s <= context_lens[s])
+ *   out          : [rows][num_q_heads][head_dim] of out_dtype (f32/f16/bf16)
+ * Other arguments as paged_attention_decode.  Supported: 16-bit caches ((bf16, bf16),
+ * (f16, f16)); head_dim 64 or 128; block_size 16 or 32; group size 1..16.  Other cache
+ * dtypes return PKV_ERR_DTYPE.  No workspace.  Preconditions (unchecked on the device):
+ * n_s <= max_q_len and n_s <= context_lens[s]; block IDs in range for the tokens read.
+ */
+int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                            const int32_t* cu_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
+                            const pkv_cache_desc* cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                            float scale, void* out, pkv_dtype out_dtype, hipStream_t stream);
+
 /* ---------------------------------------------------------------- block moves ---
  * Whole physical blocks of one layer's K and V caches (block_bytes = num_kv_heads *
  * block_size * head_dim * element bytes each).  IDs are int32 device arrays; a

@@ -26,7 +26,7 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHA
 EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_schedule",
             "paged_attention_workspace_size", "paged_attention_decode", "paged_attention_decode_window",
             "paged_attention_shared_prefix_workspace_size", "paged_attention_decode_shared_prefix",
-            "paged_kv_copy_blocks", "paged_kv_swap_out", "paged_kv_swap_in",
+            "paged_attention_prefill", "paged_kv_copy_blocks", "paged_kv_swap_out", "paged_kv_swap_in",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_alloc", "pkv_pool_share", "pkv_pool_release",
             "pkv_pool_cow", "pkv_pool_free_count", "pkv_pool_refcount",
             "pkv_status_string", "pkv_abi_version"]
@@ -90,6 +90,10 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
                                                          vp, i32, i32, vp, i32, f32, vp, ctypes.c_int,
                                                          vp, ctypes.c_size_t, vp]
     lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
+    lib.paged_attention_prefill.argtypes = [vp, ctypes.c_int, i32, i32, vp, i32, vp, vp,
+                                            ctypes.POINTER(CacheDesc), vp, i32, vp, i32, f32, vp,
+                                            ctypes.c_int, vp]
+    lib.paged_attention_prefill.restype = ctypes.c_int
     lib.paged_kv_copy_blocks.argtypes = [vp, vp, i32, vp, vp, ctypes.POINTER(CacheDesc), vp]
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     lib.paged_kv_swap_out.argtypes = [vp, i32, vp, vp, ctypes.POINTER(CacheDesc), vp, vp, vp]
@@ -201,6 +205,26 @@ def paged_kv_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check("paged_kv_write",
            lib.paged_kv_write(_ptr(slot_mapping), slot_mapping.numel(), _ptr(k), _ptr(v), src,
                               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def paged_attention_prefill(q: torch.Tensor, cu_q: torch.Tensor, max_q_len: int, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            scale: float, out: torch.Tensor, max_context_len: int, q_dtype=None,
+                            out_dtype=None, stream=None) -> torch.Tensor:
+    """Chunked-prefill attention into `out` ([rows][H_q][D]); see include/pagedkv.h."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    rows, hq, d = q.shape
+    assert cu_q.dtype == torch.int32 and block_tables.dtype == torch.int32
+    assert context_lens.dtype == torch.int32
+    _check("paged_attention_prefill",
+           lib.paged_attention_prefill(
+               _ptr(q), dtype_code(q_dtype if q_dtype is not None else q.dtype), cu_q.numel() - 1, hq,
+               _ptr(cu_q), int(max_q_len), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+               _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
+               float(scale), _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
+               _stream(stream)))
+    return out
 
 
 def paged_kv_copy_blocks(src_ids: torch.Tensor, dst_ids: torch.Tensor, k_cache: torch.Tensor,

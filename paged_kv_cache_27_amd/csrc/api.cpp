@@ -142,11 +142,41 @@ int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
   return PKV_OK;
 }
 
+// Arguments common to both uses of the rows kernel; the use-specific ones stay null.
+pkv::RowsArgs rows_args(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                        const void* v_cache, const pkv_cache_desc* c, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, float scale, int32_t tiles, hipStream_t stream) {
+  pkv::RowsArgs p;
+  p.q = q;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = c->num_kv_heads;
+  p.head_dim = c->head_dim;
+  p.block_size = c->block_size;
+  p.cache_dtype = c->dtype;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.scale = scale;
+  p.tiles = tiles;
+  p.stream = stream;
+  p.group_starts = nullptr;
+  p.prefix_lens = nullptr;
+  p.pre_part = nullptr;
+  p.splits = 1;
+  p.cu_q = nullptr;
+  p.context_lens = nullptr;
+  p.out = nullptr;
+  p.out_dtype = 0;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 5; }
+int32_t pkv_abi_version(void) { return 6; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -392,25 +422,13 @@ int paged_attention_decode_shared_prefix(
 
   float* pre_part = (float*)((char*)workspace + plan.sk.ws_bytes);
   if (max_prefix_len > 0) {
-    pkv::PrefixArgs p;
-    p.q = q;
-    p.num_seqs = num_seqs;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = cache->num_kv_heads;
-    p.head_dim = cache->head_dim;
-    p.block_size = cache->block_size;
-    p.cache_dtype = cache->dtype;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.block_tables = block_tables;
-    p.max_blocks_per_seq = max_blocks_per_seq;
+    pkv::RowsArgs p = rows_args(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                                max_blocks_per_seq, scale, plan.tiles, stream);
     p.group_starts = group_starts;
     p.prefix_lens = prefix_lens;
-    p.scale = scale;
     p.pre_part = pre_part;
     p.splits = plan.splits;
-    p.tiles = plan.tiles;
-    hipError_t e = pkv::launch_prefix(p, num_groups, stream);
+    hipError_t e = pkv::launch_prefix(p, num_groups);
     if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
     if (e != hipSuccess) return PKV_ERR_LAUNCH;
   }
@@ -448,6 +466,33 @@ int paged_attention_decode_shared_prefix(
   a.pre_part = pre_part;
   a.pre_splits = plan.splits;
   hipError_t e = pkv::launch_decode_streamk(a, stream);
+  if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                            const int32_t* cu_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
+                            const pkv_cache_desc* cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                            float scale, void* out, pkv_dtype out_dtype, hipStream_t stream) {
+  int st = check_decode_shape(cache, q_dtype, out_dtype, num_seqs, num_q_heads, max_context_len);
+  if (st) return st;
+  if (cache->dtype != PKV_BF16 && cache->dtype != PKV_F16) return PKV_ERR_DTYPE;
+  if (max_q_len < 0 || max_q_len > max_context_len || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!q || !cu_q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
+  const int32_t G = num_q_heads / cache->num_kv_heads;
+  const int64_t tiles = ((int64_t)max_q_len * G + pkv::kPrefixRows - 1) / pkv::kPrefixRows;
+  if (tiles * num_seqs * cache->num_kv_heads > 0x7fffffff) return PKV_ERR_SHAPE;
+  pkv::RowsArgs p = rows_args(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                              max_blocks_per_seq, scale, (int32_t)tiles, stream);
+  p.cu_q = cu_q;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.out_dtype = out_dtype;
+  hipError_t e = pkv::launch_prefill(p);
   if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }

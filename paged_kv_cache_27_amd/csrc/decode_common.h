@@ -137,15 +137,6 @@ template <> struct Qk<kF32, kF32> {
 
 template <int Q> struct QBytes { static constexpr int v = DtInfo<Q>::bytes; };
 
-__device__ __forceinline__ void store_out(void* out, size_t idx, int out_dtype, float x) {
-  if (out_dtype == kF32)
-    ((float*)out)[idx] = x;
-  else if (out_dtype == kBF16)
-    ((uint16_t*)out)[idx] = f32_to_bf16_rne(x);
-  else
-    ((uint16_t*)out)[idx] = f32_to_f16_rne(x);
-}
-
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

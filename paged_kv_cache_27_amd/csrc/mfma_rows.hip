@@ -1,21 +1,29 @@
-// Shared-prefix decode for gfx950: the prefix half of cascade attention.
+// Attention of many query rows against one paged token range, on the matrix cores
+// (gfx950).  Two uses:
 //
-// With prefix caching several sequences map their first blocks to the same physical
-// blocks ("La despensa por casilleros", section "Prefix caching: compartir casilleros
-// con copy-on-write"; "PagedAttention por dentro...", section "Compartir prefijos").
-// Attention over those shared tokens is the same matrix product for every sequence of
-// the group, so it is computed once for all of them: the queries of the group's
-// sequences (for one KV head: n_seqs x G rows) are the rows of
-//   S = Q K^T,  P = online-softmax(S),  O = P V
-// over the prefix tokens, and each row leaves a partial result (running max m in the
-// log2 domain, denominator l, unnormalised output acc) that the suffix pass merges
-// with the sequence's own tokens by the log-sum-exp algebra of the online softmax
-// ("Optimizacion de Inferencia LLM", sections "PagedAttention: Conceptos de SO..."
-// and "FlashAttention-3...").
+// Shared-prefix decode (the prefix half of cascade attention).  With prefix caching
+// several sequences map their first blocks to the same physical blocks ("La despensa
+// por casilleros", section "Prefix caching: compartir casilleros con copy-on-write";
+// "PagedAttention por dentro...", section "Compartir prefijos").  Attention over those
+// shared tokens is the same matrix product for every sequence of the group, so it is
+// computed once for all of them: the queries of the group's sequences (for one KV head:
+// n_seqs x G rows) are the rows of S = Q K^T, P = online-softmax(S), O = P V over the
+// prefix tokens, and each row leaves a partial result (running max m in the log2
+// domain, denominator l, unnormalised output acc) that the suffix pass merges with the
+// sequence's own tokens by the log-sum-exp algebra of the online softmax ("Optimizacion
+// de Inferencia LLM", sections "PagedAttention: Conceptos de SO..." and
+// "FlashAttention-3...").
 //
-// One workgroup = 8 waves x 16 query rows of one (group, KV head), over one slice of
-// the prefix's 16-token chunks (the slices are merged later with the suffix).  Per
-// chunk and wave, on the matrix cores:
+// Chunked prefill.  A sequence brings a chunk of n query tokens, the last n of its
+// context (their K/V already written); query i, at position ctx - n + i, attends to
+// tokens 0 .. ctx - n + i of the paged cache ("PagedAttention por dentro...", section
+// "Chunked prefill integrado con paged KV"; "Componentes Internos de Servicio de vLLM",
+// section "Chunked prefill protege la cola del TTFT").  The rows are (query token,
+// query head) of one sequence and KV head, each with its own causal limit, and the
+// workgroup writes the normalised output.
+//
+// One workgroup = 4 waves x 16 query rows, over a range of the 16-token chunks.  Per
+// chunk and wave:
 //   * S^T = K Q^T: 16x16x32 MFMAs, A = the K tile rows as loaded (lane l: token l%16,
 //     8 dims), B = the wave's 16 query rows; lane l gets row l%16 against tokens
 //     4(l/16) .. 4(l/16)+3;
@@ -27,8 +35,9 @@
 //     fragment is one conflict-free 8-byte LDS read.
 // K tiles are staged in LDS the same way (row stride padded by 16 bytes, so a wave's
 // 16-byte A-fragment reads hit distinct banks); the loads of the next chunks are in
-// flight in registers while one is computed.  Workgroups of one KV head are placed on
-// one XCD (workgroup i runs on XCD i mod 8) so the head's shared tiles stay in that L2.
+// flight in registers while one is computed.  Workgroups of one KV head are numbered
+// so that they share an XCD (workgroup i runs on XCD i mod 8 when the KV head count is a
+// multiple of 8), keeping the head's K/V tiles in that L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,25 +97,25 @@ __device__ __forceinline__ float pf_xor32_sum(float x) {
   return bits_f32(r[0]) + bits_f32(r[1]);
 }
 
-constexpr int kPfxWaves = kPrefixRows / 16;
-constexpr int kPfxRows = kPrefixRows;
-#ifndef PKV_PFX_DEPTH
-#define PKV_PFX_DEPTH 3
+constexpr int kRowsWaves = kPrefixRows / 16;
+#ifndef PKV_ROWS_DEPTH
+#define PKV_ROWS_DEPTH 3
 #endif
-constexpr int PD = PKV_PFX_DEPTH;  // chunks whose loads are in flight
+constexpr int kRowsDepth = PKV_ROWS_DEPTH;  // chunks whose loads are in flight
 constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay <= 2^8 between rescales
 // Four workgroups of four waves per CU (four waves per SIMD, <= 128 VGPRs each): a
 // workgroup waits at its per-chunk barrier while the others compute.
-constexpr int kPfxWavesPerSimd = 4;
+constexpr int kRowsWavesPerSimd = 4;
 
-template <int KV, int D>
-__global__ void __launch_bounds__(64 * kPfxWaves) __attribute__((amdgpu_waves_per_eu(kPfxWavesPerSimd)))
-prefix_kernel(const PrefixArgs a) {
+// PREFILL = false: shared-prefix partials; true: causal chunked prefill.
+template <int KV, int D, bool PREFILL>
+__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(kRowsWavesPerSimd)))
+rows_kernel(const RowsArgs a) {
   using O_ = PfxOps<KV>;
   constexpr int ROW = 2 * D;          // bytes of one K/V row
   constexpr int NKC = D / 32;         // 16x16x32 MFMAs per chunk (K dims)
   constexpr int NJ = D / 16;          // 16-dim output tiles
-  constexpr int NT = 64 * kPfxWaves;   // threads of the workgroup
+  constexpr int NT = 64 * kRowsWaves;  // threads of the workgroup
   constexpr int KSTAGE = 16 * (D / 8); // threads staging K: 16 rows x D/8 16-byte pieces
   constexpr int VSTAGE = 4 * (D / 2);  // threads staging V: 4 token groups x D/2 dim pairs
   // V is staged by threads VOFF .. VOFF + VSTAGE - 1: the threads after the K stagers
@@ -121,23 +130,43 @@ prefix_kernel(const PrefixArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][4 * D * 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int Hkv = a.num_kv_heads, G = a.num_q_heads / Hkv, T = a.splits;
+  const int Hkv = a.num_kv_heads, G = a.num_q_heads / Hkv;
   int bid = blockIdx.x;
   const int g = bid % Hkv;
   bid /= Hkv;
-  const int t = bid % T;
-  bid /= T;
-  const int tile = bid % a.tiles;
-  const int j = bid / a.tiles;
-  const int s0 = a.group_starts[j], s1 = a.group_starts[j + 1];
-  const int nrows = (s1 - s0) * G;
-  const int row0 = tile * kPfxRows;
-  if (row0 >= nrows) return;          // whole workgroup: no barrier reached
-  const int P = a.prefix_lens[s0];
-  if (P <= 0) return;                 // nothing shared: the suffix pass reads no partial
-  const int nch = P / 16;
-  const int c0 = nch * t / T, c1 = nch * (t + 1) / T;
-  const int32_t* bt = a.block_tables + (size_t)s0 * a.max_blocks_per_seq;
+  // ---- this workgroup's rows, their sequence and the chunk range [c0, c1)
+  int T = 1, t = 0, s, nrows, c0, c1, qbase, row0, base_pos = 0, ctx = 0;
+  if constexpr (PREFILL) {
+    // rows (query token i, head) of sequence s: row r -> token r / G, head g G + r % G
+    row0 = (bid % a.tiles) * kPrefixRows;
+    s = bid / a.tiles;
+    const int n = a.cu_q[s + 1] - a.cu_q[s];
+    nrows = n * G;
+    if (row0 >= nrows) return;  // whole workgroup: no barrier reached
+    ctx = a.context_lens[s];
+    base_pos = ctx - n;         // position of query token 0
+    qbase = a.cu_q[s];
+    const int last = min(nrows, row0 + kPrefixRows) - 1;
+    c0 = 0;
+    c1 = (base_pos + last / G + 1 + 15) / 16;  // through the last row's own token
+  } else {
+    // rows (sequence, head) of group j: row r -> sequence s0 + r / G, head g G + r % G
+    T = a.splits;
+    t = bid % T;
+    bid /= T;
+    row0 = (bid % a.tiles) * kPrefixRows;
+    const int j = bid / a.tiles;
+    s = a.group_starts[j];
+    nrows = (a.group_starts[j + 1] - s) * G;
+    if (row0 >= nrows) return;  // whole workgroup: no barrier reached
+    const int P = a.prefix_lens[s];
+    if (P <= 0) return;         // nothing shared: the suffix pass reads no partial
+    const int nch = P / 16;
+    c0 = nch * t / T;
+    c1 = nch * (t + 1) / T;
+    qbase = s;
+  }
+  const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const int BS = a.block_size;
   const uint8_t* kc = (const uint8_t*)a.k_cache;
   const uint8_t* vc = (const uint8_t*)a.v_cache;
@@ -147,12 +176,14 @@ prefix_kernel(const PrefixArgs a) {
   const int rq = row0 + 16 * wv + (lane & 15);
   const bool qvalid = rq < nrows;
   const uint8_t* qrow = (const uint8_t*)a.q +
-      ((size_t)(s0 + (qvalid ? rq / G : 0)) * a.num_q_heads + g * G + (qvalid ? rq % G : 0)) * ROW;
+      ((size_t)(qbase + (qvalid ? rq / G : 0)) * a.num_q_heads + g * G + (qvalid ? rq % G : 0)) * ROW;
   typename O_::frag8 qf[NKC];
 #pragma unroll
   for (int c = 0; c < NKC; ++c)
     qf[c] = qvalid ? __builtin_bit_cast(typename O_::frag8, *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4))))
                    : __builtin_bit_cast(typename O_::frag8, make_uint4(0, 0, 0, 0));
+  // prefill: this row attends to tokens < lim (its own position included)
+  const int lim = PREFILL ? base_pos + (qvalid ? rq / G : 0) + 1 : 0;
 
   float m = kNegInf, l = 0.0f;
   f32x4_t O[NJ];
@@ -175,7 +206,7 @@ prefix_kernel(const PrefixArgs a) {
     uint4 k;
     uint32_t v[4];
   };
-  // live == false: padding past the slice, reads nothing.
+  // live == false: padding past the range, reads nothing.
   auto issue = [&](int c, bool live, Stage& st) {
     const size_t off = tile_off(min(c, c1 - 1));
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc + off, live && kstage ? 16 * ROW : 0);
@@ -184,21 +215,27 @@ prefix_kernel(const PrefixArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) st.v[e] = load_kv4<false>(vrs, (4 * tg + e) * ROW + 4 * dp);
   };
-  auto stage = [&](int buf, const Stage& st) {
+  // Chunk c's tiles into LDS buffer buf.  Prefill: V rows past the context (the tail of
+  // its last block: any bytes, NaN included) are staged as zeros, so that their zero
+  // weights cannot turn into NaN; K rows there only meet masked scores.
+  auto stage = [&](int buf, int c, const Stage& st) {
     if (kstage) *(uint4*)&lds_k[buf][kr * KROW + 8 * kp] = st.k;
     if (vstage) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (!PREFILL || 16 * c + 4 * tg + e < ctx) ? st.v[e] : 0u;
       // dim 2dp: the low halves of the 4 tokens' words, dim 2dp+1: the high halves
-      const uint32_t lo01 = __builtin_amdgcn_perm(st.v[1], st.v[0], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(st.v[3], st.v[2], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(st.v[1], st.v[0], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(st.v[3], st.v[2], 0x07060302u);
+      const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
       uint16_t* base = &lds_v[buf][(tg * D + 2 * dp) * 4];
       *(uint2*)base = make_uint2(lo01, lo23);
       *(uint2*)(base + 4) = make_uint2(hi01, hi23);
     }
   };
   // One chunk from LDS buffer buf: S^T = K Q^T, online softmax, O += P V.
-  auto compute = [&](int buf) {
+  auto compute = [&](int buf, int c) {
     // A = K rows: lane l reads token l%16, dims 32cc + 8(l/16); S^T lane l: row l%16
     // against tokens 4(l/16) + i
     f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -209,13 +246,18 @@ prefix_kernel(const PrefixArgs a) {
     }
     float sv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = S[i] * scale_l2;
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = S[i] * scale_l2;
+      if (PREFILL && 16 * c + 4 * (lane >> 4) + i >= lim) sv[i] = kNegInf;  // causal mask
+    }
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = pf_xor32_max(pf_xor16_max(bm));  // finite: every prefix token is a real token
+    // every row's first chunk holds a token it attends to (prefix: all; prefill: token
+    // 0), so m is finite from the first chunk on
+    bm = pf_xor32_max(pf_xor16_max(bm));
     // Lazy rescaling: the reference max m moves only when a score exceeds it by more than
     // kRescaleSlack (and on the first chunk, m = -inf), so weights 2^(s - m) stay <= 2^8.
     // (m, l, acc) stay one consistent partial -- l and acc are sums of 2^(s - m) for the
-    // same m -- so the log-sum-exp merge is unchanged; only the rare rescale remains.
+    // same m -- so the log-sum-exp algebra is unchanged; only the rare rescale remains.
     const bool move = bm > m + kRescaleSlack;
     if (__ballot(move) != 0) {
       const float mn = move ? bm : m;
@@ -249,59 +291,86 @@ prefix_kernel(const PrefixArgs a) {
 
   // Chunks c0 .. c1-1 with the loads of the next PD chunks in flight (a register ring,
   // rotated by a fully unrolled inner loop; every step issues its loads unconditionally,
-  // padding ones through an empty resource), staged in LDS one chunk ahead.
+  // padding ones through an empty resource), staged in LDS one chunk ahead.  Prefill keeps
+  // one chunk less in flight: its causal mask costs the registers of one ring slot.
+  constexpr int PD = PREFILL ? kRowsDepth - 1 : kRowsDepth;
   if (c0 < c1) {
     const int n = c1 - c0;
     Stage ring[PD];
 #pragma unroll
     for (int u = 0; u < PD; ++u) issue(c0 + u, u < n, ring[u]);
-    stage(0, ring[0]);
+    stage(0, c0, ring[0]);
     __syncthreads();
     for (int i = 0; i < n; i += PD) {
 #pragma unroll
       for (int u = 0; u < PD; ++u) {
         const int ii = i + u;
         if (ii >= n) break;
-        compute(ii & 1);
-        if (ii + 1 < n) stage((ii + 1) & 1, ring[(u + 1) % PD]);
+        compute(ii & 1, c0 + ii);
+        if (ii + 1 < n) stage((ii + 1) & 1, c0 + ii + 1, ring[(u + 1) % PD]);
         issue(c0 + ii + PD, ii + PD < n, ring[u]);
         __syncthreads();
       }
     }
   }
 
-  // ---- partials: m, l per row (lanes 0..15), acc rows 4(l/16) + i, dims 16jj + l%16
-  const float lsum = pf_xor32_sum(pf_xor16_sum(l));
-  auto part_of = [&](int rr) {
-    return a.pre_part + (((size_t)(s0 + rr / G) * a.num_q_heads + g * G + rr % G) * T + t) * STRIDE;
-  };
-  if (lane < 16 && qvalid) {
-    float* pp = part_of(rq);
-    pp[0] = m;
-    pp[1] = lsum;
-  }
+  const float lsum = pf_xor32_sum(pf_xor16_sum(l));  // row l%16's denominator
+  if constexpr (PREFILL) {
+    // ---- output rows 4(l/16) + i, dims 16jj + l%16: acc / l of that row (held by lane
+    // 4(l/16) + i), rounded to the output dtype
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
-    if (rr >= nrows) continue;
-    float* pp = part_of(rr) + 4;
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(lsum, 4 * (lane >> 4) + i);
+      const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
+      if (rr >= nrows) continue;
+      const float inv = li != 0.0f ? 1.0f / li : 0.0f;
+      const size_t o = ((size_t)(qbase + rr / G) * a.num_q_heads + g * G + rr % G) * D + (lane & 15);
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) pp[16 * jj + (lane & 15)] = O[jj][i];
+      for (int jj = 0; jj < NJ; ++jj) store_out(a.out, o + 16 * jj, a.out_dtype, O[jj][i] * inv);
+    }
+  } else {
+    // ---- partials: m, l per row (lanes 0..15), acc rows 4(l/16) + i, dims 16jj + l%16
+    auto part_of = [&](int rr) {
+      return a.pre_part + (((size_t)(qbase + rr / G) * a.num_q_heads + g * G + rr % G) * T + t) * STRIDE;
+    };
+    if (lane < 16 && qvalid) {
+      float* pp = part_of(rq);
+      pp[0] = m;
+      pp[1] = lsum;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
+      if (rr >= nrows) continue;
+      float* pp = part_of(rr) + 4;
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) pp[16 * jj + (lane & 15)] = O[jj][i];
+    }
   }
 }
 
 // ---- dispatch --------------------------------------------------------------------
-hipError_t launch_prefix(const PrefixArgs& a, int num_groups, hipStream_t stream) {
-  const dim3 grid((unsigned)num_groups * a.tiles * a.splits * a.num_kv_heads);
-  const dim3 block(64 * kPfxWaves);
-#define PKV_PFX(KV, D) hipLaunchKernelGGL((prefix_kernel<KV, D>), grid, block, 0, stream, a)
-  if (a.cache_dtype == kBF16 && a.head_dim == 128) PKV_PFX(kBF16, 128);
-  else if (a.cache_dtype == kBF16 && a.head_dim == 64) PKV_PFX(kBF16, 64);
-  else if (a.cache_dtype == kF16 && a.head_dim == 128) PKV_PFX(kF16, 128);
-  else if (a.cache_dtype == kF16 && a.head_dim == 64) PKV_PFX(kF16, 64);
+template <bool PREFILL>
+static hipError_t launch_rows(const RowsArgs& a, int64_t grid) {
+  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 block(64 * kRowsWaves);
+#define PKV_ROWS(KV, D) \
+  hipLaunchKernelGGL((rows_kernel<KV, D, PREFILL>), dim3((unsigned)grid), block, 0, a.stream, a)
+  if (a.cache_dtype == kBF16 && a.head_dim == 128) PKV_ROWS(kBF16, 128);
+  else if (a.cache_dtype == kBF16 && a.head_dim == 64) PKV_ROWS(kBF16, 64);
+  else if (a.cache_dtype == kF16 && a.head_dim == 128) PKV_ROWS(kF16, 128);
+  else if (a.cache_dtype == kF16 && a.head_dim == 64) PKV_ROWS(kF16, 64);
   else return hipErrorInvalidValue;
-#undef PKV_PFX
+#undef PKV_ROWS
   return hipGetLastError();
+}
+
+hipError_t launch_prefix(const RowsArgs& a, int num_groups) {
+  return launch_rows<false>(a, (int64_t)num_groups * a.tiles * a.splits * a.num_kv_heads);
+}
+
+hipError_t launch_prefill(const RowsArgs& a) {
+  return launch_rows<true>(a, (int64_t)a.num_seqs * a.tiles * a.num_kv_heads);
 }
 
 }  // namespace pkv

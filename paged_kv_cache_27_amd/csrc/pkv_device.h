@@ -97,6 +97,16 @@ __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32 rounds to nearest even
 }
 
+// out[idx] = x rounded to nearest-even in the output dtype (f32 / bf16 / f16).
+__device__ __forceinline__ void store_out(void* out, size_t idx, int out_dtype, float x) {
+  if (out_dtype == kF32)
+    ((float*)out)[idx] = x;
+  else if (out_dtype == kBF16)
+    ((uint16_t*)out)[idx] = f32_to_bf16_rne(x);
+  else
+    ((uint16_t*)out)[idx] = f32_to_f16_rne(x);
+}
+
 // fp32 -> OCP e4m3fn, round to nearest even, saturating to +-448 (infinities
 // included), NaN -> NaN.  Pure integer arithmetic on the fp32 bit pattern.
 __device__ __forceinline__ uint32_t f32_to_e4m3_satfinite(float y) {

@@ -54,8 +54,9 @@ struct DecodeArgs {
   int32_t pre_splits;
 };
 
-// Shared-prefix (cascade) pass: partials of every group's shared prefix.
-struct PrefixArgs {
+// Many query rows against one paged token range on the matrix cores (mfma_rows.hip):
+// the shared-prefix pass (partials of every group's shared prefix) and chunked prefill.
+struct RowsArgs {
   const void* q;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
   int cache_dtype;
@@ -63,15 +64,23 @@ struct PrefixArgs {
   const void* v_cache;
   const int32_t* block_tables;
   int32_t max_blocks_per_seq;
+  float scale;
+  int32_t tiles;                // kPrefixRows-row tiles per group / per sequence
+  hipStream_t stream;
+  // shared prefix
   const int32_t* group_starts;  // [groups + 1]
   const int32_t* prefix_lens;   // [N]
-  float scale;
   float* pre_part;              // [N][H_q][splits][4 + D]: m, l, pad, pad, acc
   int32_t splits;               // slices of each prefix's chunks
-  int32_t tiles;                // kPrefixRows-row tiles per group
+  // chunked prefill
+  const int32_t* cu_q;          // [N + 1]: query rows of sequence s are cu_q[s] .. cu_q[s+1]-1
+  const int32_t* context_lens;  // [N], counting the chunk
+  void* out;                    // [rows][H_q][D]
+  int out_dtype;
 };
-constexpr int kPrefixRows = 64;  // query rows per workgroup of the prefix kernel
-hipError_t launch_prefix(const PrefixArgs& a, int num_groups, hipStream_t stream);
+constexpr int kPrefixRows = 64;  // query rows per workgroup of the rows kernel
+hipError_t launch_prefix(const RowsArgs& a, int num_groups);
+hipError_t launch_prefill(const RowsArgs& a);
 
 // Whole-block moves (copy-on-write, swap): pair i moves block src_ids[i] (row i when
 // src_ids is null) of each of the K and V sources to block dst_ids[i] (row i when

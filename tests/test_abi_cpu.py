@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pkv.pkv_abi_version() == 5
+    assert pkv.pkv_abi_version() == 6
 
 
 def test_workspace_header_constant_matches_header():

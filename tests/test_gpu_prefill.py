@@ -1,0 +1,95 @@
+"""Chunked-prefill attention over the paged cache vs the oracle, through the C ABI (GPU
+only).  Each sequence's chunk is the last n_s tokens of its context (written to the
+cache first, with the same write kernel), and query i attends to tokens 0 .. its own
+position.  Bar: 4e-3 * max(1, |ref|) element by element."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_27_amd as pkv
+from gpu_helpers import GpuStep, assert_close_to_oracle, out_to_f64, to_device, torch_dtype
+from helpers import oracle_step
+from workloads import LLAMA8B, PREFIX, TINY, make_workload, prefill_queries
+
+pytestmark = pytest.mark.gpu
+THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.load_library()
+
+
+def _run(orc, cfg, chunk_lens, seed=77):
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    c = w.cfg
+    q, cu = prefill_queries(w, chunk_lens, seed)
+    out = torch.empty((int(cu[-1]), c.num_q_heads, c.head_dim), dtype=torch_dtype(c.out_dtype), device="cuda")
+    pkv.paged_attention_prefill(to_device(q, c.q_dtype), torch.from_numpy(cu).cuda(), int(np.max(chunk_lens)),
+                                g.k_cache, g.v_cache, g.block_tables, g.context_lens, w.scale, out,
+                                w.max_context_len)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    del g
+    kc, vc, _, _ = oracle_step(orc, w, pairs=np.zeros((0, 2), np.int32))
+    ref = orc.prefill(q, c.q_dtype, cu, kc, vc, c.kv_dtype, w.block_tables, w.context_lens, w.scale,
+                      threads=THREADS)
+    return w, q, cu, got, ref
+
+
+CTX = (20, 77, 130, 300, 513, 64)
+CASES = {
+    "bf16-ragged": (LLAMA8B, CTX, (1, 16, 17, 64, 100, 64)),
+    "bf16-whole-prompts": (LLAMA8B, CTX, CTX),
+    "f16-d64-mha": (TINY.replace(name="f16-mha", num_q_heads=4, num_kv_heads=4, head_dim=64, q_dtype="f16",
+                                 kv_dtype="f16", src_dtype="f16", out_dtype="f16", pool_blocks=0),
+                    (33, 90, 7, 200), (33, 45, 7, 130)),
+    "mqa-g8-f32out": (LLAMA8B.replace(name="mqa", num_q_heads=8, num_kv_heads=1, out_dtype="f32"),
+                      (150, 48), (150, 20)),
+    "g16-b32": (PREFIX.replace(name="g16", num_q_heads=32, num_kv_heads=2, ctx_kind="fixed"), (300, 97, 33),
+                (96, 97, 5)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_prefill_matches_oracle(orc, name):
+    base, ctx, n = CASES[name]
+    cfg = base.replace(num_seqs=len(ctx), ctx_kind="fixed", ctx_params=tuple(ctx))
+    print(f"prefill case {name}: ctx {ctx} chunks {n}", flush=True)
+    w, _, _, got, ref = _run(orc, cfg, n)
+    assert_close_to_oracle(got, ref, w.cfg.kv_dtype, name)
+
+
+def test_one_token_chunks_match_decode(orc):
+    """A chunk of one token per sequence computes what decode computes (the two kernels
+    agree within the bar; each against the oracle)."""
+    cfg = LLAMA8B.replace(num_seqs=5, ctx_kind="fixed", ctx_params=(1, 15, 16, 17, 260))
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    c = w.cfg
+    cu = np.arange(c.num_seqs + 1, dtype=np.int32)
+    out = torch.empty_like(g.out)
+    pkv.paged_attention_prefill(g.q, torch.from_numpy(cu).cuda(), 1, g.k_cache, g.v_cache, g.block_tables,
+                                g.context_lens, w.scale, out, w.max_context_len)
+    dec = g.decode(0)
+    torch.cuda.synchronize()
+    _, _, _, ref = oracle_step(orc, w)
+    assert_close_to_oracle(out_to_f64(out), ref, "bf16", "prefill n=1")
+    assert (out.float() - dec.float()).abs().max().item() <= 8e-3
+
+
+def test_prefill_full_size(orc):
+    """The chunked-prefill workload at full size: 8 sequences, each a 512-token chunk at
+    the end of a 4096-token context (Llama-3-8B-shaped heads), every output."""
+    cfg = LLAMA8B.replace(num_seqs=8, ctx_kind="fixed", ctx_params=(4096,) * 8)
+    print("prefill full size: 8 x 512 at 4096", flush=True)
+    w, _, _, got, ref = _run(orc, cfg, (512,) * 8)
+    assert_close_to_oracle(got, ref, "bf16", "prefill full size")
