@@ -358,6 +358,63 @@ def measure_block_moves(args):
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def measure_prefill(args):
+    """Chunked prefill: 8 sequences, each a 512-token chunk ending a 4096-token context
+    (Llama-3-8B-shaped heads, bf16).  Algorithmic flops: per query head and attended
+    (query, token) pair, 2 d for q.k and 2 d for p v; MFMA-bound."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_27_amd as pkv
+    from workloads import LLAMA8B, POISON_BITS, cache_shape, make_workload, prefill_queries
+
+    cfg = LLAMA8B.replace(name="prefill-8x512-at-4096-bf16", num_seqs=8, ctx_kind="fixed",
+                          ctx_params=(4096,) * 8)
+    w = make_workload(cfg)
+    c = cfg
+    n = np.full(c.num_seqs, 512, np.int32)
+    q_np, cu_np = prefill_queries(w, n)
+    dev = "cuda"
+    k = torch.full(cache_shape(w), POISON_BITS["bf16"], dtype=torch.int16, device=dev).view(torch.bfloat16)
+    v = torch.full(cache_shape(w), POISON_BITS["bf16"], dtype=torch.int16, device=dev).view(torch.bfloat16)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    ctx = torch.from_numpy(w.context_lens).to(dev)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    hs = torch.from_numpy(w.hist_seq).to(dev)
+    hp = torch.from_numpy(w.hist_pos).to(dev)
+    slots = pkv.paged_kv_slot_mapping(hs, hp, bt, c.block_size)
+    pkv.paged_kv_write(slots, up(w.hist_k), up(w.hist_v), k, v)
+    ns = pkv.paged_kv_slot_mapping(torch.from_numpy(w.new_seq).to(dev), torch.from_numpy(w.new_pos).to(dev), bt,
+                                   c.block_size)
+    pkv.paged_kv_write(ns, up(w.new_k), up(w.new_v), k, v)
+    q = up(q_np)
+    cu = torch.from_numpy(cu_np).to(dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    call = lambda: pkv.paged_attention_prefill(q, cu, 512, k, v, bt, ctx, w.scale, out, w.max_context_len)
+    for _ in range(3):
+        call()
+    flush = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.reps)]
+    for e0, e1 in ev:
+        sink.copy_(flush.sum())
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    pairs = sum(int(x) - 512 + i + 1 for x in w.context_lens for i in range(512))
+    flops = pairs * c.num_q_heads * c.head_dim * 4
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {"workload": cfg.name, "flops": flops, "ms_cold_mean": ms, "TFLOPs": tflops,
+           "frac_mfma_bf16_peak": tflops / MFMA_BF16_PEAK_TFLOPS}
+    log(f"[{cfg.name}] {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
+        f"the bf16 MFMA peak), {flops / 1e9:.1f} GFLOP")
+    return res
+
+
 def cpu_baseline(w, budget_s):
     """The fp64 oracle on this host's cores over whole sequences (all query heads), taken
     in order until the wall budget is spent."""
@@ -435,6 +492,7 @@ def main():
                 del s2
                 torch.cuda.empty_cache()
     blocks = measure_block_moves(args) if args.all else None
+    prefill = measure_prefill(args) if args.all else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -465,7 +523,7 @@ def main():
     if args.json_out:
         Path(args.json_out).parent.mkdir(parents=True, exist_ok=True)
         Path(args.json_out).write_text(json.dumps({"headline": res, "others": others, "block_moves": blocks,
-                                                   "cpu": cpu}, indent=1))
+                                                   "prefill": prefill, "cpu": cpu}, indent=1))
     print(json.dumps(line), flush=True)
 
 

@@ -22,22 +22,23 @@
 // query head) of one sequence and KV head, each with its own causal limit, and the
 // workgroup writes the normalised output.
 //
-// One workgroup = 4 waves x 16 query rows, over a range of the 16-token chunks.  Per
-// chunk and wave:
-//   * S^T = K Q^T: 16x16x32 MFMAs, A = the K tile rows as loaded (lane l: token l%16,
-//     8 dims), B = the wave's 16 query rows; lane l gets row l%16 against tokens
-//     4(l/16) .. 4(l/16)+3;
-//   * that is exactly the A operand of the 16x16x16 P.V MFMA (row l%16, k = tokens
-//     4(l/16)+i), so P never leaves registers (split hi + lo in 16 bits, ~16 bits of
-//     each probability kept);
-//   * V's B operand needs 4 consecutive tokens of one dim per lane: the workgroup
-//     stages each V tile once in LDS as [4-token group][dim][4 tokens], so a lane's
-//     fragment is one conflict-free 8-byte LDS read.
-// K tiles are staged in LDS the same way (row stride padded by 16 bytes, so a wave's
-// 16-byte A-fragment reads hit distinct banks); the loads of the next chunks are in
-// flight in registers while one is computed.  Workgroups of one KV head are numbered
-// so that they share an XCD (workgroup i runs on XCD i mod 8 when the KV head count is a
-// multiple of 8), keeping the head's K/V tiles in that L2.
+// One workgroup = 4 waves x 16 query rows, over a range of the 16-token chunks, taken
+// two at a time (32-token steps).  Per step and wave, on the matrix cores:
+//   * S^T = K Q^T per chunk: 16x16x32 MFMAs, A = the chunk's K rows as staged (lane l:
+//     token l%16, 8 dims), B = the wave's 16 query rows; lane l gets row l%16 against
+//     tokens 4(l/16) .. 4(l/16)+3 of each chunk;
+//   * those 8 probabilities are exactly lane l's A operand of a 16x16x32 P.V MFMA (row
+//     l%16, k-slots 8(l/16) .. +7 standing for tokens 4(l/16)+i of both chunks), so P
+//     never leaves registers (split hi + lo in 16 bits, ~16 bits of each probability
+//     kept);
+//   * V's B operand needs those 8 tokens of one dim per lane: the workgroup stages each
+//     step's V once in LDS as [lane group][dim][8 tokens], so a lane's fragment is one
+//     conflict-free 16-byte LDS read.
+// K is staged in LDS as [32 tokens][d_h + 8] (the padding puts a wave's 16-byte
+// A-fragment reads in distinct banks); the next step's loads are in flight in registers
+// while one is computed.  Workgroups of one KV head are numbered so that they share an
+// XCD (workgroup i runs on XCD i mod 8 when the KV head count is a multiple of 8),
+// keeping the head's K/V tiles in that L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,12 +50,8 @@ namespace pkv {
 template <int KV> struct PfxOps;
 template <> struct PfxOps<kBF16> {
   using frag8 = bf16x8_t;
-  typedef __bf16 frag4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
   __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static f32x4_t pv(frag4 a, frag4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
   }
   // p = hi + lo: hi the upper half of p's fp32 bits, lo the bf16 truncation of the rest
   __device__ __forceinline__ static uint32_t hi16(float p) { return f32_bits(p) >> 16; }
@@ -64,12 +61,8 @@ template <> struct PfxOps<kBF16> {
 };
 template <> struct PfxOps<kF16> {
   using frag8 = f16x8_t;
-  typedef _Float16 frag4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
   __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static f32x4_t pv(frag4 a, frag4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
   __device__ __forceinline__ static uint32_t hi16(float p) {
     return __builtin_bit_cast(uint16_t, (_Float16)p);
@@ -98,36 +91,38 @@ __device__ __forceinline__ float pf_xor32_sum(float x) {
 }
 
 constexpr int kRowsWaves = kPrefixRows / 16;
-#ifndef PKV_ROWS_DEPTH
-#define PKV_ROWS_DEPTH 3
-#endif
-constexpr int kRowsDepth = PKV_ROWS_DEPTH;  // chunks whose loads are in flight
 constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay <= 2^8 between rescales
 // Four workgroups of four waves per CU (four waves per SIMD, <= 128 VGPRs each): a
-// workgroup waits at its per-chunk barrier while the others compute.
+// workgroup waits at its per-step barrier while the others compute.
 constexpr int kRowsWavesPerSimd = 4;
+constexpr int kRowsDepth = 1;  // steps (32 tokens each) whose loads are in flight
 
 // PREFILL = false: shared-prefix partials; true: causal chunked prefill.
+//
+// A step is two 16-token chunks A and B (B may be padding past the range).  Lane l of a
+// wave holds the scores of its row l%16 against tokens 4(l/16) + i of A and of B
+// (i < 4), and those 8 probabilities are its k-slots 8(l/16) .. 8(l/16)+7 of the
+// 16x16x32 P.V MFMA (the contraction order is free as long as V uses the same one), so
+// V is staged as [lane group g][dim][tokens 4g..4g+3 of A, 4g..4g+3 of B].
 template <int KV, int D, bool PREFILL>
 __global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(kRowsWavesPerSimd)))
 rows_kernel(const RowsArgs a) {
   using O_ = PfxOps<KV>;
-  constexpr int ROW = 2 * D;          // bytes of one K/V row
-  constexpr int NKC = D / 32;         // 16x16x32 MFMAs per chunk (K dims)
-  constexpr int NJ = D / 16;          // 16-dim output tiles
-  constexpr int NT = 64 * kRowsWaves;  // threads of the workgroup
-  constexpr int KSTAGE = 16 * (D / 8); // threads staging K: 16 rows x D/8 16-byte pieces
-  constexpr int VSTAGE = 4 * (D / 2);  // threads staging V: 4 token groups x D/2 dim pairs
-  // V is staged by threads VOFF .. VOFF + VSTAGE - 1: the threads after the K stagers
-  // when both fit in the workgroup, else the same threads (each then stages both)
-  constexpr int VOFF = KSTAGE + VSTAGE <= NT ? KSTAGE : 0;
-  constexpr int KROW = D + 8;          // K row stride in LDS (elements): conflict-free A reads
-  constexpr int STRIDE = 4 + D;        // floats per partial: m, l, pad, pad, acc[D]
-  static_assert(KSTAGE <= NT && VOFF + VSTAGE <= NT && KSTAGE % 64 == 0 && VOFF % 64 == 0,
-                "K and V staged by whole waves of the workgroup");
-  // K tile as [token][KROW], V tile as [token group tg][dim d][token 4tg + e], 16-bit.
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][16 * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][4 * D * 4];
+  using frag8 = typename O_::frag8;
+  constexpr int ROW = 2 * D;           // bytes of one K/V row
+  constexpr int NKC = D / 32;          // 16x16x32 MFMAs per 16 tokens of Q.K (K dims)
+  constexpr int NJ = D / 16;           // 16-dim output tiles
+  constexpr int NT = 64 * kRowsWaves;   // threads of the workgroup
+  constexpr int KPIECES = 32 * (D / 8); // 16-byte pieces of a step's 32 K rows
+  constexpr int KP = KPIECES / NT;      // K pieces per thread (2 for D = 128, 1 for 64)
+  constexpr int VSTAGE = 4 * (D / 2);   // V stagers: 4 lane groups x D/2 dim pairs
+  constexpr int KROW = D + 8;           // K row stride in LDS (elements): conflict-free A reads
+  constexpr int STRIDE = 4 + D;         // floats per partial: m, l, pad, pad, acc[D]
+  static_assert(KP >= 1 && KPIECES % NT == 0 && VSTAGE <= NT && VSTAGE % 64 == 0,
+                "staging by whole waves of the workgroup");
+  // K as [32 tokens][KROW]; V as [lane group g][dim][8 tokens: 4g..4g+3 of A, of B], 16-bit.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][32 * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][4 * D * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int Hkv = a.num_kv_heads, G = a.num_q_heads / Hkv;
@@ -177,91 +172,132 @@ rows_kernel(const RowsArgs a) {
   const bool qvalid = rq < nrows;
   const uint8_t* qrow = (const uint8_t*)a.q +
       ((size_t)(qbase + (qvalid ? rq / G : 0)) * a.num_q_heads + g * G + (qvalid ? rq % G : 0)) * ROW;
-  typename O_::frag8 qf[NKC];
+  frag8 qf[NKC];
 #pragma unroll
   for (int c = 0; c < NKC; ++c)
-    qf[c] = qvalid ? __builtin_bit_cast(typename O_::frag8, *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4))))
-                   : __builtin_bit_cast(typename O_::frag8, make_uint4(0, 0, 0, 0));
-  // prefill: this row attends to tokens < lim (its own position included)
-  const int lim = PREFILL ? base_pos + (qvalid ? rq / G : 0) + 1 : 0;
+    qf[c] = qvalid ? __builtin_bit_cast(frag8, *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4))))
+                   : __builtin_bit_cast(frag8, make_uint4(0, 0, 0, 0));
+  // this row attends to tokens < lim (prefill: its own position included; prefix: the
+  // range's end, so a padding chunk B past it is masked)
+  const int lim = PREFILL ? base_pos + (qvalid ? rq / G : 0) + 1 : 16 * c1;
+  // the smallest limit of the wave's rows (rows grow with the query token): steps below
+  // it need no mask
+  const int lim_lo = PREFILL ? __builtin_amdgcn_readfirstlane(base_pos + min(row0 + 16 * wv, nrows - 1) / G + 1)
+                             : 16 * c1;
 
   float m = kNegInf, l = 0.0f;
   f32x4_t O[NJ];
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj) O[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  const int bs_shift = BS == 32 ? 5 : 4;  // block size 16 or 32
   auto tile_off = [&](int c) {  // byte offset of chunk c's (block, KV head) rows
     const int tok = 16 * c;
-    const int blk = bt[tok / BS];
-    return (((size_t)blk * Hkv + g) * BS + (tok % BS)) * ROW;
+    const int blk = bt[tok >> bs_shift];
+    return (((size_t)blk * Hkv + g) * BS + (tok & (BS - 1))) * ROW;
   };
-  // Staging threads: 0..KSTAGE-1 copy one 16-byte piece of the K tile (row kr, piece kp);
-  // VOFF..VOFF+VSTAGE-1 one dim pair of 4 V tokens (tokens 4tg .. 4tg+3, dims 2dp, 2dp+1).
-  // Every thread issues both loads, the ones it has no part in through an empty resource.
-  const int kr = (tid / (D / 8)) & 15, kp = tid % (D / 8);
-  const int vt = tid - VOFF;
-  const int tg = (vt / (D / 2)) & 3, dp = (vt & 0xffff) % (D / 2);
-  const bool kstage = tid < KSTAGE, vstage = vt >= 0 && vt < VSTAGE;
+  // Staging: K piece q = tid + NT k (k < KP) is row q / (D/8) (chunk A for rows < 16, B
+  // after), 16-byte piece q % (D/8); V stager (gg, dp) = (tid / (D/2), tid % (D/2))
+  // loads tokens 4gg .. 4gg+3 of A and of B, dims 2dp, 2dp+1.  Every thread issues all
+  // its loads, the ones it has no part in through an empty resource.
+  const int gg = (tid / (D / 2)) & 3, dp = tid % (D / 2);
+  const bool vstage = tid < VSTAGE;
   struct Stage {
-    uint4 k;
-    uint32_t v[4];
+    uint4 k[KP];
+    uint32_t v[8];
   };
-  // live == false: padding past the range, reads nothing.
-  auto issue = [&](int c, bool live, Stage& st) {
-    const size_t off = tile_off(min(c, c1 - 1));
-    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc + off, live && kstage ? 16 * ROW : 0);
-    const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vc + off, live && vstage ? 16 * ROW : 0);
-    st.k = load_kv16<false>(krs, kr * ROW + 16 * kp);
+  // Step at chunk cA (chunks cA, cA + 1): live halves read, padding ones read nothing.
+  auto issue = [&](int cA, Stage& st) {
+    const bool la = cA < c1, lb = cA + 1 < c1;
+    const size_t oa = tile_off(min(cA, c1 - 1)), ob = tile_off(min(cA + 1, c1 - 1));
+    const __amdgpu_buffer_rsrc_t ka = tile_rsrc(kc + oa, la ? 16 * ROW : 0);
+    const __amdgpu_buffer_rsrc_t kb = tile_rsrc(kc + ob, lb ? 16 * ROW : 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st.v[e] = load_kv4<false>(vrs, (4 * tg + e) * ROW + 4 * dp);
+    for (int k = 0; k < KP; ++k) {
+      const int q = tid + NT * k, r = q / (D / 8), pc = q % (D / 8);
+      // rows < 16 are chunk A: a whole wave's rows fall in one chunk, so the choice is
+      // made on the first lane's row (a scalar select of the two resources)
+      const bool in_a = __builtin_amdgcn_readfirstlane(r) < 16;
+      st.k[k] = load_kv16<false>(in_a ? ka : kb, (r & 15) * ROW + 16 * pc);
+    }
+    const __amdgpu_buffer_rsrc_t va = tile_rsrc(vc + oa, la && vstage ? 16 * ROW : 0);
+    const __amdgpu_buffer_rsrc_t vb = tile_rsrc(vc + ob, lb && vstage ? 16 * ROW : 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      st.v[e] = load_kv4<false>(va, (4 * gg + e) * ROW + 4 * dp);
+      st.v[4 + e] = load_kv4<false>(vb, (4 * gg + e) * ROW + 4 * dp);
+    }
   };
-  // Chunk c's tiles into LDS buffer buf.  Prefill: V rows past the context (the tail of
+  // Step at chunk cA into LDS buffer buf.  Prefill: V rows past the context (the tail of
   // its last block: any bytes, NaN included) are staged as zeros, so that their zero
   // weights cannot turn into NaN; K rows there only meet masked scores.
-  auto stage = [&](int buf, int c, const Stage& st) {
-    if (kstage) *(uint4*)&lds_k[buf][kr * KROW + 8 * kp] = st.k;
-    if (vstage) {
-      uint32_t w[4];
+  auto stage = [&](int buf, int cA, const Stage& st) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (!PREFILL || 16 * c + 4 * tg + e < ctx) ? st.v[e] : 0u;
-      // dim 2dp: the low halves of the 4 tokens' words, dim 2dp+1: the high halves
-      const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-      uint16_t* base = &lds_v[buf][(tg * D + 2 * dp) * 4];
-      *(uint2*)base = make_uint2(lo01, lo23);
-      *(uint2*)(base + 4) = make_uint2(hi01, hi23);
+    for (int k = 0; k < KP; ++k) {
+      const int q = tid + NT * k, r = q / (D / 8), pc = q % (D / 8);
+      *(uint4*)&lds_k[buf][r * KROW + 8 * pc] = st.k[k];
+    }
+    if (vstage) {
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = st.v[e];
+      if (PREFILL && 16 * (cA + 2) > ctx) {  // the step that holds the context's end
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (16 * (cA + e / 4) + 4 * gg + (e & 3) >= ctx) w[e] = 0u;
+      }
+      // dim 2dp: the low halves of the 8 tokens' words, dim 2dp+1: the high halves
+      const uint4 lo = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                                  __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
+                                  __builtin_amdgcn_perm(w[5], w[4], 0x05040100u),
+                                  __builtin_amdgcn_perm(w[7], w[6], 0x05040100u));
+      const uint4 hi = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                                  __builtin_amdgcn_perm(w[3], w[2], 0x07060302u),
+                                  __builtin_amdgcn_perm(w[5], w[4], 0x07060302u),
+                                  __builtin_amdgcn_perm(w[7], w[6], 0x07060302u));
+      uint16_t* base = &lds_v[buf][(gg * D + 2 * dp) * 8];
+      *(uint4*)base = lo;
+      *(uint4*)(base + 8) = hi;
     }
   };
-  // One chunk from LDS buffer buf: S^T = K Q^T, online softmax, O += P V.
-  auto compute = [&](int buf, int c) {
-    // A = K rows: lane l reads token l%16, dims 32cc + 8(l/16); S^T lane l: row l%16
-    // against tokens 4(l/16) + i
-    f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+  // One step from LDS buffer buf: S^T = K Q^T for chunks A and B, online softmax over
+  // their 32 tokens, O += P V.
+  auto compute = [&](int buf, int cA) {
+    // A = K rows: lane l reads token l%16 of a chunk, dims 32cc + 8(l/16)
+    f32x4_t SA = {0.0f, 0.0f, 0.0f, 0.0f}, SB = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int cc = 0; cc < NKC; ++cc) {
-      const uint4 kf = *(const uint4*)&lds_k[buf][(lane & 15) * KROW + 32 * cc + 8 * (lane >> 4)];
-      S = O_::qk(__builtin_bit_cast(typename O_::frag8, kf), qf[cc], S);
+      const uint4 ka = *(const uint4*)&lds_k[buf][(lane & 15) * KROW + 32 * cc + 8 * (lane >> 4)];
+      const uint4 kb = *(const uint4*)&lds_k[buf][(16 + (lane & 15)) * KROW + 32 * cc + 8 * (lane >> 4)];
+      SA = O_::qk(__builtin_bit_cast(frag8, ka), qf[cc], SA);
+      SB = O_::qk(__builtin_bit_cast(frag8, kb), qf[cc], SB);
     }
-    float sv[4];
+    float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = S[i] * scale_l2;
-      if (PREFILL && 16 * c + 4 * (lane >> 4) + i >= lim) sv[i] = kNegInf;  // causal mask
+      sv[i] = SA[i] * scale_l2;
+      sv[4 + i] = SB[i] * scale_l2;
     }
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    // every row's first chunk holds a token it attends to (prefix: all; prefill: token
-    // 0), so m is finite from the first chunk on
+    if (16 * cA + 32 > lim_lo) {  // a step reaching some row's limit: mask its tokens past it
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ta = 16 * cA + 4 * (lane >> 4) + i;
+        if (ta >= lim) sv[i] = kNegInf;  // causal mask / range end
+        if (ta + 16 >= lim) sv[4 + i] = kNegInf;
+      }
+    }
+    float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    // every row's first step holds a token it attends to (prefix: all of chunk A;
+    // prefill: token 0), so m is finite from the first step on
     bm = pf_xor32_max(pf_xor16_max(bm));
     // Lazy rescaling: the reference max m moves only when a score exceeds it by more than
-    // kRescaleSlack (and on the first chunk, m = -inf), so weights 2^(s - m) stay <= 2^8.
+    // kRescaleSlack (and on the first step, m = -inf), so weights 2^(s - m) stay <= 2^8.
     // (m, l, acc) stay one consistent partial -- l and acc are sums of 2^(s - m) for the
     // same m -- so the log-sum-exp algebra is unchanged; only the rare rescale remains.
     const bool move = bm > m + kRescaleSlack;
     if (__ballot(move) != 0) {
       const float mn = move ? bm : m;
-      const float alpha = fast_exp2(m - mn);  // 0 on the first chunk, 1 for rows kept
+      const float alpha = fast_exp2(m - mn);  // 0 on the first step, 1 for rows kept
       l *= alpha;
       m = mn;
       // O rows 4(l/16) + i take the factor of row 4(l/16) + i, held by lane 4(l/16) + i
@@ -272,33 +308,39 @@ rows_kernel(const RowsArgs a) {
         for (int jj = 0; jj < NJ; ++jj) O[jj][i] *= ai;
       }
     }
-    float p[4];
+    float p[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    const uint32_t h0 = O_::hi16(p[0]) | (O_::hi16(p[1]) << 16), h1 = O_::hi16(p[2]) | (O_::hi16(p[3]) << 16);
-    const uint32_t l0 = O_::lo16(p[0]) | (O_::lo16(p[1]) << 16), l1 = O_::lo16(p[2]) | (O_::lo16(p[3]) << 16);
-    const auto ahi = __builtin_bit_cast(typename O_::frag4, make_uint2(h0, h1));
-    const auto alo = __builtin_bit_cast(typename O_::frag4, make_uint2(l0, l1));
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sv[i] - m);
+    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hw[i] = O_::hi16(p[2 * i]) | (O_::hi16(p[2 * i + 1]) << 16);
+      lw[i] = O_::lo16(p[2 * i]) | (O_::lo16(p[2 * i + 1]) << 16);
+    }
+    const frag8 ahi = __builtin_bit_cast(frag8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    const frag8 alo = __builtin_bit_cast(frag8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
-      const uint2 vv = *(const uint2*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 4];
-      const auto vf = __builtin_bit_cast(typename O_::frag4, vv);
-      O[jj] = O_::pv(ahi, vf, O[jj]);
-      O[jj] = O_::pv(alo, vf, O[jj]);
+      const uint4 vv = *(const uint4*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 8];
+      const frag8 vf = __builtin_bit_cast(frag8, vv);
+      O[jj] = O_::qk(ahi, vf, O[jj]);
+      O[jj] = O_::qk(alo, vf, O[jj]);
     }
   };
 
-  // Chunks c0 .. c1-1 with the loads of the next PD chunks in flight (a register ring,
-  // rotated by a fully unrolled inner loop; every step issues its loads unconditionally,
-  // padding ones through an empty resource), staged in LDS one chunk ahead.  Prefill keeps
-  // one chunk less in flight: its causal mask costs the registers of one ring slot.
-  constexpr int PD = PREFILL ? kRowsDepth - 1 : kRowsDepth;
+  // Steps at chunks c0, c0 + 2, ... < c1.  Step k's loads go to ring slot k % PD, and
+  // its tiles to LDS buffer k & 1.  At step ii: the loads of step ii + PD are issued into
+  // the slot step ii vacated (staged one step earlier), step ii is computed from LDS
+  // while they and the other steps' loads are in flight, then step ii + 1 is staged from
+  // its slot.  Every step issues its loads unconditionally, padding ones through an
+  // empty resource; the ring is rotated by a fully unrolled inner loop.
+  constexpr int PD = kRowsDepth;
   if (c0 < c1) {
-    const int n = c1 - c0;
+    const int n = (c1 - c0 + 1) / 2;  // steps
     Stage ring[PD];
 #pragma unroll
-    for (int u = 0; u < PD; ++u) issue(c0 + u, u < n, ring[u]);
+    for (int u = 0; u < PD; ++u) issue(c0 + 2 * u, ring[u]);
     stage(0, c0, ring[0]);
     __syncthreads();
     for (int i = 0; i < n; i += PD) {
@@ -306,9 +348,9 @@ rows_kernel(const RowsArgs a) {
       for (int u = 0; u < PD; ++u) {
         const int ii = i + u;
         if (ii >= n) break;
-        compute(ii & 1, c0 + ii);
-        if (ii + 1 < n) stage((ii + 1) & 1, c0 + ii + 1, ring[(u + 1) % PD]);
-        issue(c0 + ii + PD, ii + PD < n, ring[u]);
+        issue(c0 + 2 * (ii + PD), ring[u]);
+        compute(ii & 1, c0 + 2 * ii);
+        if (ii + 1 < n) stage((ii + 1) & 1, c0 + 2 * (ii + 1), ring[(u + 1) % PD]);
         __syncthreads();
       }
     }
