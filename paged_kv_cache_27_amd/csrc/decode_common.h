@@ -739,43 +739,51 @@ __device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int st
 // Log-sum-exp merge of P partial results of one query head (the online-softmax
 // algebra: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p),
 // by one workgroup of kMergeThreads threads: thread t handles output dim t % D for
-// the partials p = t / D, t / D + PG, ...; the PG groups are combined in LDS.
-// part(p) returns the partial's (m, l, acc-row) pointers.  vnorm scales the result
-// (the fp8 V scale).  Returns nothing; writes out[row + d].
+// the partials p = t / D, t / D + PG, ...; the PG groups are combined in LDS.  One
+// pass with a running maximum (each partial rescales the running sums when it raises
+// it); a thread's partials are read in batches of kMergeBatch, so it waits for memory
+// once per batch.  part(p) returns the partial's (m, l, acc-row) pointers.  vnorm
+// scales the result (the fp8 V scale).  Writes out[row + d].
 constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 8;
+__device__ __forceinline__ void lse_add(float& M, float& L, float& A, float m, float l, float x) {
+  const float Mn = fmaxf(M, m);
+  const float base = Mn == kNegInf ? 0.0f : Mn;
+  const float fo = fast_exp2(M - base), fn = fast_exp2(m - base);
+  L = L * fo + l * fn;
+  A = A * fo + x * fn;
+  M = Mn;
+}
 template <int D, class PartFn>
 __device__ __forceinline__ void merge_head(int P, PartFn part, void* out, size_t row, int out_dtype,
                                            float vnorm) {
   constexpr int PG = kMergeThreads / D;
   __shared__ float red_m[PG], red_l[PG], red_a[PG][D];
   const int t = threadIdx.x, d = t % D, pg = t / D;
-  float M = kNegInf;
-#pragma unroll 4
-  for (int p = pg; p < P; p += PG) M = fmaxf(M, *part(p).m);
-  if (d == 0) red_m[pg] = M;
-  __syncthreads();
+  float M = kNegInf, L = 0.0f, A = 0.0f;
+  for (int p0 = pg; p0 < P; p0 += PG * kMergeBatch) {
+    float pm[kMergeBatch], pl[kMergeBatch], pa[kMergeBatch];
 #pragma unroll
-  for (int j = 0; j < PG; ++j) M = fmaxf(M, red_m[j]);
-  float L = 0.0f, A = 0.0f;
-  if (M != kNegInf) {
-#pragma unroll 4
-    for (int p = pg; p < P; p += PG) {
-      const auto q = part(p);
-      const float f = fast_exp2(*q.m - M);
-      L += f * *q.l;
-      A += f * q.acc[d];
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int p = p0 + b * PG;
+      const auto q = part(p < P ? p : p0);
+      pm[b] = p < P ? *q.m : kNegInf;  // past the last partial: weighs nothing
+      pl[b] = *q.l;
+      pa[b] = q.acc[d];
     }
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) lse_add(M, L, A, pm[b], pl[b], pa[b]);
   }
   red_a[pg][d] = A;
-  if (d == 0) red_l[pg] = L;
+  if (d == 0) {
+    red_m[pg] = M;
+    red_l[pg] = L;
+  }
   __syncthreads();
   if (pg == 0) {
-    float LL = 0.0f, AA = 0.0f;
+    float MM = kNegInf, LL = 0.0f, AA = 0.0f;
 #pragma unroll
-    for (int j = 0; j < PG; ++j) {
-      LL += red_l[j];
-      AA += red_a[j][d];
-    }
+    for (int j = 0; j < PG; ++j) lse_add(MM, LL, AA, red_m[j], red_l[j], red_a[j][d]);
     store_out(out, row + d, out_dtype, LL != 0.0f ? AA / LL * vnorm : 0.0f);
   }
 }
