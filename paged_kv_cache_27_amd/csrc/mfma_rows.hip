@@ -48,46 +48,46 @@
 namespace pkv {
 
 template <int KV> struct PfxOps;
+// split2(p0, p1, hi, lo): two probabilities as 16-bit pairs (p0 in the low half) with
+// p = hi + lo to ~16 significant bits; kOne: 1.0 in both halves.
 template <> struct PfxOps<kBF16> {
   using frag8 = bf16x8_t;
+  static constexpr uint32_t kOne = 0x3f803f80u;
   __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  // p = hi + lo: hi the upper half of p's fp32 bits, lo the bf16 truncation of the rest
-  __device__ __forceinline__ static uint32_t hi16(float p) { return f32_bits(p) >> 16; }
-  __device__ __forceinline__ static uint32_t lo16(float p) {
-    return f32_bits(p - bits_f32(f32_bits(p) & 0xffff0000u)) >> 16;
+  // hi: the upper halves of the fp32 bits; lo: the upper half of what remains
+  __device__ __forceinline__ static void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t b0 = f32_bits(p0), b1 = f32_bits(p1);
+    hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+    const float r0 = p0 - bits_f32(b0 & 0xffff0000u), r1 = p1 - bits_f32(b1 & 0xffff0000u);
+    lo = __builtin_amdgcn_perm(f32_bits(r1), f32_bits(r0), 0x07060302u);
   }
 };
 template <> struct PfxOps<kF16> {
   using frag8 = f16x8_t;
+  static constexpr uint32_t kOne = 0x3c003c00u;
   __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static uint32_t hi16(float p) {
-    return __builtin_bit_cast(uint16_t, (_Float16)p);
-  }
-  __device__ __forceinline__ static uint32_t lo16(float p) {
-    const _Float16 h = (_Float16)p;
-    return __builtin_bit_cast(uint16_t, (_Float16)(p - (float)h));
+  // hi rounded toward zero to f16, lo the rest (also f16)
+  __device__ __forceinline__ static void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
   }
 };
 
+// NaN-propagating maximum (v_maximum3_f32 on gfx950: no operand canonicalisation, and
+// three inputs per instruction); scores here are finite or -inf.
+__device__ __forceinline__ float pf_max(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 __device__ __forceinline__ float pf_xor16_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
-  return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+  return pf_max(bits_f32(r[0]), bits_f32(r[1]));
 }
 __device__ __forceinline__ float pf_xor32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
-  return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
-}
-__device__ __forceinline__ float pf_xor16_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
-  return bits_f32(r[0]) + bits_f32(r[1]);
-}
-__device__ __forceinline__ float pf_xor32_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
-  return bits_f32(r[0]) + bits_f32(r[1]);
+  return pf_max(bits_f32(r[0]), bits_f32(r[1]));
 }
 
 constexpr int kRowsWaves = kPrefixRows / 16;
@@ -163,9 +163,18 @@ rows_kernel(const RowsArgs a) {
   }
   const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const int BS = a.block_size;
-  const uint8_t* kc = (const uint8_t*)a.k_cache;
-  const uint8_t* vc = (const uint8_t*)a.v_cache;
-  const float scale_l2 = a.scale * kLog2e;
+  // this KV head's rows of block 0; a block's rows for all heads span blk_bytes
+  const size_t head_off = (size_t)g * BS * ROW;
+  const uint8_t* kc = (const uint8_t*)a.k_cache + head_off;
+  const uint8_t* vc = (const uint8_t*)a.v_cache + head_off;
+  const uint32_t blk_bytes = (uint32_t)Hkv * (uint32_t)(BS * ROW);
+  // Scores are taken raw (S = K Q^T) and scaled inside the exponent, 2^(c s - m) with
+  // c = |scale| log2(e) > 0, so the running max can be taken on raw scores: a negative
+  // scale flips the sign of Q instead (exact in 16 bits) and a zero scale zeroes Q (all
+  // scores 0: the same uniform weights).
+  const float c_l2 = (a.scale != 0.0f ? __builtin_fabsf(a.scale) : 1.0f) * kLog2e;
+  const uint32_t qflip = a.scale < 0.0f ? 0x80008000u : 0u;
+  const bool qzero = a.scale == 0.0f;
 
   // ---- this lane's query row (B operand of S^T = K Q^T: row l%16, dims 8(l/16) + 32c)
   const int rq = row0 + 16 * wv + (lane & 15);
@@ -174,9 +183,14 @@ rows_kernel(const RowsArgs a) {
       ((size_t)(qbase + (qvalid ? rq / G : 0)) * a.num_q_heads + g * G + (qvalid ? rq % G : 0)) * ROW;
   frag8 qf[NKC];
 #pragma unroll
-  for (int c = 0; c < NKC; ++c)
-    qf[c] = qvalid ? __builtin_bit_cast(frag8, *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4))))
-                   : __builtin_bit_cast(frag8, make_uint4(0, 0, 0, 0));
+  for (int c = 0; c < NKC; ++c) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (qvalid && !qzero) {
+      w = *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4)));
+      w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
+    }
+    qf[c] = __builtin_bit_cast(frag8, w);
+  }
   // this row attends to tokens < lim (prefill: its own position included; prefix: the
   // range's end, so a padding chunk B past it is masked)
   const int lim = PREFILL ? base_pos + (qvalid ? rq / G : 0) + 1 : 16 * c1;
@@ -185,22 +199,27 @@ rows_kernel(const RowsArgs a) {
   const int lim_lo = PREFILL ? __builtin_amdgcn_readfirstlane(base_pos + min(row0 + 16 * wv, nrows - 1) / G + 1)
                              : 16 * c1;
 
-  float m = kNegInf, l = 0.0f;
-  f32x4_t O[NJ];
+  // m: the row's reference max (log2 domain, scaled); O: unnormalised output rows
+  // 4(l/16) + i, dims 16jj + l%16; Ol: the same rows' denominators, summed on the matrix
+  // cores as P times a ones tile (every column holds the row sum)
+  float m = kNegInf;
+  f32x4_t O[NJ], Ol = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj) O[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const frag8 ones = __builtin_bit_cast(frag8, make_uint4(O_::kOne, O_::kOne, O_::kOne, O_::kOne));
 
   const int bs_shift = BS == 32 ? 5 : 4;  // block size 16 or 32
-  auto tile_off = [&](int c) {  // byte offset of chunk c's (block, KV head) rows
+  auto tile_off = [&](int c) {  // byte offset of chunk c's rows from kc / vc
     const int tok = 16 * c;
-    const int blk = bt[tok >> bs_shift];
-    return (((size_t)blk * Hkv + g) * BS + (tok & (BS - 1))) * ROW;
+    const uint32_t blk = (uint32_t)bt[tok >> bs_shift];
+    return (size_t)blk * blk_bytes + (uint32_t)((tok & (BS - 1)) * ROW);
   };
   // Staging: K piece q = tid + NT k (k < KP) is row q / (D/8) (chunk A for rows < 16, B
   // after), 16-byte piece q % (D/8); V stager (gg, dp) = (tid / (D/2), tid % (D/2))
   // loads tokens 4gg .. 4gg+3 of A and of B, dims 2dp, 2dp+1.  Every thread issues all
   // its loads, the ones it has no part in through an empty resource.
   const int gg = (tid / (D / 2)) & 3, dp = tid % (D / 2);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const bool vstage = tid < VSTAGE;
   struct Stage {
     uint4 k[KP];
@@ -215,9 +234,9 @@ rows_kernel(const RowsArgs a) {
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
       const int q = tid + NT * k, r = q / (D / 8), pc = q % (D / 8);
-      // rows < 16 are chunk A: a whole wave's rows fall in one chunk, so the choice is
-      // made on the first lane's row (a scalar select of the two resources)
-      const bool in_a = __builtin_amdgcn_readfirstlane(r) < 16;
+      // rows < 16 (pieces q < 2 D) are chunk A; 2 D is a multiple of 64, so a whole
+      // wave's pieces fall in one chunk (a scalar select of the two resources)
+      const bool in_a = 64 * wvu + NT * k < 2 * D;
       st.k[k] = load_kv16<false>(in_a ? ka : kb, (r & 15) * ROW + 16 * pc);
     }
     const __amdgpu_buffer_rsrc_t va = tile_rsrc(vc + oa, la && vstage ? 16 * ROW : 0);
@@ -272,11 +291,11 @@ rows_kernel(const RowsArgs a) {
       SA = O_::qk(__builtin_bit_cast(frag8, ka), qf[cc], SA);
       SB = O_::qk(__builtin_bit_cast(frag8, kb), qf[cc], SB);
     }
-    float sv[8];
+    float sv[8];  // raw scores
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = SA[i] * scale_l2;
-      sv[4 + i] = SB[i] * scale_l2;
+      sv[i] = SA[i];
+      sv[4 + i] = SB[i];
     }
     if (16 * cA + 32 > lim_lo) {  // a step reaching some row's limit: mask its tokens past it
 #pragma unroll
@@ -286,10 +305,12 @@ rows_kernel(const RowsArgs a) {
         if (ta + 16 >= lim) sv[4 + i] = kNegInf;
       }
     }
-    float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    float bm = pf_max(pf_max(pf_max(sv[0], sv[1]), sv[2]), pf_max(pf_max(sv[3], sv[4]), sv[5]));
+    bm = pf_max(pf_max(bm, sv[6]), sv[7]);
     // every row's first step holds a token it attends to (prefix: all of chunk A;
-    // prefill: token 0), so m is finite from the first step on
-    bm = pf_xor32_max(pf_xor16_max(bm));
+    // prefill: token 0), so m is finite from the first step on (a later step masked
+    // for the whole row gives bm = -inf, which moves nothing)
+    bm = pf_xor32_max(pf_xor16_max(bm)) * c_l2;
     // Lazy rescaling: the reference max m moves only when a score exceeds it by more than
     // kRescaleSlack (and on the first step, m = -inf), so weights 2^(s - m) stay <= 2^8.
     // (m, l, acc) stay one consistent partial -- l and acc are sums of 2^(s - m) for the
@@ -298,28 +319,26 @@ rows_kernel(const RowsArgs a) {
     if (__ballot(move) != 0) {
       const float mn = move ? bm : m;
       const float alpha = fast_exp2(m - mn);  // 0 on the first step, 1 for rows kept
-      l *= alpha;
       m = mn;
       // O rows 4(l/16) + i take the factor of row 4(l/16) + i, held by lane 4(l/16) + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ai = __shfl(alpha, 4 * (lane >> 4) + i);
+        Ol[i] *= ai;
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) O[jj][i] *= ai;
       }
     }
     float p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sv[i] - m);
-    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], c_l2, -m));
     uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hw[i] = O_::hi16(p[2 * i]) | (O_::hi16(p[2 * i + 1]) << 16);
-      lw[i] = O_::lo16(p[2 * i]) | (O_::lo16(p[2 * i + 1]) << 16);
-    }
+    for (int i = 0; i < 4; ++i) O_::split2(p[2 * i], p[2 * i + 1], hw[i], lw[i]);
     const frag8 ahi = __builtin_bit_cast(frag8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
     const frag8 alo = __builtin_bit_cast(frag8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    Ol = O_::qk(ahi, ones, Ol);
+    Ol = O_::qk(alo, ones, Ol);
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const uint4 vv = *(const uint4*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 8];
@@ -356,13 +375,12 @@ rows_kernel(const RowsArgs a) {
     }
   }
 
-  const float lsum = pf_xor32_sum(pf_xor16_sum(l));  // row l%16's denominator
   if constexpr (PREFILL) {
-    // ---- output rows 4(l/16) + i, dims 16jj + l%16: acc / l of that row (held by lane
-    // 4(l/16) + i), rounded to the output dtype
+    // ---- output rows 4(l/16) + i, dims 16jj + l%16: acc / l of that row, rounded to
+    // the output dtype
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(lsum, 4 * (lane >> 4) + i);
+      const float li = Ol[i];
       const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
       if (rr >= nrows) continue;
       const float inv = li != 0.0f ? 1.0f / li : 0.0f;
@@ -371,22 +389,20 @@ rows_kernel(const RowsArgs a) {
       for (int jj = 0; jj < NJ; ++jj) store_out(a.out, o + 16 * jj, a.out_dtype, O[jj][i] * inv);
     }
   } else {
-    // ---- partials: m, l per row (lanes 0..15), acc rows 4(l/16) + i, dims 16jj + l%16
+    // ---- partials: m per row (lanes 0..15: row l%16), l and acc of rows 4(l/16) + i
+    // (l from the lanes of column 0), acc dims 16jj + l%16
     auto part_of = [&](int rr) {
       return a.pre_part + (((size_t)(qbase + rr / G) * a.num_q_heads + g * G + rr % G) * T + t) * STRIDE;
     };
-    if (lane < 16 && qvalid) {
-      float* pp = part_of(rq);
-      pp[0] = m;
-      pp[1] = lsum;
-    }
+    if (lane < 16 && qvalid) part_of(rq)[0] = m;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
       if (rr >= nrows) continue;
-      float* pp = part_of(rr) + 4;
+      float* pp = part_of(rr);
+      if ((lane & 15) == 0) pp[1] = Ol[i];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) pp[16 * jj + (lane & 15)] = O[jj][i];
+      for (int jj = 0; jj < NJ; ++jj) pp[4 + 16 * jj + (lane & 15)] = O[jj][i];
     }
   }
 }

@@ -2,6 +2,7 @@
 only).  Each sequence's chunk is the last n_s tokens of its context (written to the
 cache first, with the same write kernel), and query i attends to tokens 0 .. its own
 position.  Bar: 4e-3 * max(1, |ref|) element by element."""
+import dataclasses
 import os
 
 import numpy as np
@@ -23,8 +24,10 @@ def _gpu():
     pkv.load_library()
 
 
-def _run(orc, cfg, chunk_lens, seed=77):
+def _run(orc, cfg, chunk_lens, seed=77, scale=None):
     w = make_workload(cfg)
+    if scale is not None:
+        w = dataclasses.replace(w, scale=scale)
     g = GpuStep(w)
     g.fill_history()
     g.write_new()
@@ -64,6 +67,16 @@ def test_prefill_matches_oracle(orc, name):
     print(f"prefill case {name}: ctx {ctx} chunks {n}", flush=True)
     w, _, _, got, ref = _run(orc, cfg, n)
     assert_close_to_oracle(got, ref, w.cfg.kv_dtype, name)
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.5])
+def test_prefill_scale_values(orc, scale):
+    """Softmax scales other than 1/sqrt(d_h): a negative one, zero (uniform weights over
+    each query's attended tokens) and a large one (sharply peaked weights)."""
+    cfg = LLAMA8B.replace(num_seqs=3, ctx_kind="fixed", ctx_params=(40, 130, 300))
+    print(f"prefill scale {scale}", flush=True)
+    w, _, _, got, ref = _run(orc, cfg, (40, 64, 33), scale=scale)
+    assert_close_to_oracle(got, ref, "bf16", f"prefill scale {scale}")
 
 
 def test_one_token_chunks_match_decode(orc):

@@ -6,6 +6,7 @@ passed to it vary independently of how the cache actually shares blocks, as long
 the declared sharing is real: the true grouping, finer groups, a shorter declared
 prefix, singleton groups without a prefix, and prefixes that cover whole contexts.
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -27,15 +28,16 @@ def _gpu():
     pkv.load_library()
 
 
-def _run(g, starts, prefix_lens, out=None, workspace=None):
+def _run(g, starts, prefix_lens, out=None, workspace=None, scale=None):
     w = g.w
+    scale = w.scale if scale is None else scale
     starts = np.asarray(starts, np.int32)
     prefix_lens = np.asarray(prefix_lens, np.int32)
     gmax = int(np.diff(starts).max())
     pmax = int(prefix_lens.max())
     out = g.out if out is None else out
     pkv.paged_attention_decode_shared_prefix(
-        g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens, w.scale, out, w.max_context_len,
+        g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens, scale, out, w.max_context_len,
         torch.from_numpy(starts).cuda(), torch.from_numpy(prefix_lens).cuda(), gmax, pmax,
         workspace=workspace)
     torch.cuda.synchronize()
@@ -78,6 +80,18 @@ def test_true_grouping_matches_oracle(orc, name):
     out = out_to_f64(_run(g, starts, pl))
     _, _, _, ref = oracle_step(orc, w, threads=THREADS)
     assert_close_to_oracle(out, ref, w.cfg.kv_dtype, name)
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0])
+def test_scale_values(orc, scale):
+    """A negative softmax scale and a zero one: the prefix partials and the suffix pass
+    must use the same log2-domain maxima for the merge to hold."""
+    w, g = _prepared(CASES["three-groups"])
+    starts, pl = _true_grouping(w)
+    print(f"shared-prefix scale {scale}", flush=True)
+    out = out_to_f64(_run(g, starts, pl, scale=scale))
+    _, _, _, ref = oracle_step(orc, dataclasses.replace(w, scale=scale), threads=THREADS)
+    assert_close_to_oracle(out, ref, w.cfg.kv_dtype, f"scale {scale}")
 
 
 def test_declared_groupings(orc):
