@@ -22,18 +22,24 @@
 // query head) of one sequence and KV head, each with its own causal limit, and the
 // workgroup writes the normalised output.
 //
-// One workgroup = 4 waves x 16 query rows, over a range of the 16-token chunks, taken
-// two at a time (32-token steps).  Per step and wave, on the matrix cores:
+// One workgroup = 4 waves x 2 sets of 16 query rows, over a range of the 16-token
+// chunks, taken two at a time (32-token steps).  Per step, wave and row set, on the
+// matrix cores:
 //   * S^T = K Q^T per chunk: 16x16x32 MFMAs, A = the chunk's K rows as staged (lane l:
-//     token l%16, 8 dims), B = the wave's 16 query rows; lane l gets row l%16 against
-//     tokens 4(l/16) .. 4(l/16)+3 of each chunk;
+//     token l%16, 8 dims; one LDS read serves both sets), B = the set's 16 query rows;
+//     lane l gets row l%16 against tokens 4(l/16) .. 4(l/16)+3 of each chunk;
 //   * those 8 probabilities are exactly lane l's A operand of a 16x16x32 P.V MFMA (row
 //     l%16, k-slots 8(l/16) .. +7 standing for tokens 4(l/16)+i of both chunks), so P
 //     never leaves registers (split hi + lo in 16 bits, ~16 bits of each probability
 //     kept);
 //   * V's B operand needs those 8 tokens of one dim per lane: the workgroup stages each
 //     step's V once in LDS as [lane group][dim][8 tokens], so a lane's fragment is one
-//     conflict-free 16-byte LDS read.
+//     conflict-free 16-byte LDS read (again serving both sets);
+//   * the row sums come from the same P times a tile of ones.
+// Two row sets per wave halve the LDS reads, staging and barriers per MFMA against one
+// set, and give each wave two independent softmax chains (measured 9% faster on the
+// chunked-prefill workload at ~170 VGPRs, two waves per SIMD, than one set at ~110 VGPRs
+// and four waves per SIMD).
 // K is staged in LDS as [32 tokens][d_h + 8] (the padding puts a wave's 16-byte
 // A-fragment reads in distinct banks); the next step's loads are in flight in registers
 // while one is computed.  Workgroups of one KV head are numbered so that they share an
@@ -90,11 +96,14 @@ __device__ __forceinline__ float pf_xor32_max(float x) {
   return pf_max(bits_f32(r[0]), bits_f32(r[1]));
 }
 
-constexpr int kRowsWaves = kPrefixRows / 16;
+constexpr int kRowsWaves = 4;
+// Each wave owns kRowSets sets of 16 query rows: one step's K and V fragments, read once
+// from LDS, feed the MFMAs of every set, and the sets' softmax chains are independent.
+constexpr int kRowSets = kPrefixRows / (16 * kRowsWaves);
 constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay <= 2^8 between rescales
-// Four workgroups of four waves per CU (four waves per SIMD, <= 128 VGPRs each): a
-// workgroup waits at its per-step barrier while the others compute.
-constexpr int kRowsWavesPerSimd = 4;
+// Two workgroups of four waves per CU (two waves per SIMD, <= 256 VGPRs each): a
+// workgroup waits at its per-step barrier while the other computes.
+constexpr int kRowsWavesPerSimd = 2;
 constexpr int kRowsDepth = 1;  // steps (32 tokens each) whose loads are in flight
 
 // PREFILL = false: shared-prefix partials; true: causal chunked prefill.
@@ -176,43 +185,63 @@ rows_kernel(const RowsArgs a) {
   const uint32_t qflip = a.scale < 0.0f ? 0x80008000u : 0u;
   const bool qzero = a.scale == 0.0f;
 
-  // ---- this lane's query row (B operand of S^T = K Q^T: row l%16, dims 8(l/16) + 32c)
-  const int rq = row0 + 16 * wv + (lane & 15);
-  const bool qvalid = rq < nrows;
-  const uint8_t* qrow = (const uint8_t*)a.q +
-      ((size_t)(qbase + (qvalid ? rq / G : 0)) * a.num_q_heads + g * G + (qvalid ? rq % G : 0)) * ROW;
-  frag8 qf[NKC];
+  // ---- this lane's query row in each set rs (B operand of S^T = K Q^T: row l%16 of the
+  // set, dims 8(l/16) + 32c); the wave's rows are row0 + 16 (RS wv + rs) + 0..15
+  constexpr int RS = kRowSets;
+  const int wrow0 = row0 + 16 * RS * wv;
+  int rq[RS], lim[RS];
+  bool qvalid[RS];
+  frag8 qf[RS][NKC];
 #pragma unroll
-  for (int c = 0; c < NKC; ++c) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (qvalid && !qzero) {
-      w = *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4)));
-      w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
+  for (int rs = 0; rs < RS; ++rs) {
+    rq[rs] = wrow0 + 16 * rs + (lane & 15);
+    qvalid[rs] = rq[rs] < nrows;
+    const uint8_t* qrow = (const uint8_t*)a.q +
+        ((size_t)(qbase + (qvalid[rs] ? rq[rs] / G : 0)) * a.num_q_heads + g * G + (qvalid[rs] ? rq[rs] % G : 0)) * ROW;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (qvalid[rs] && !qzero) {
+        w = *(const uint4*)(qrow + 2 * (32 * c + 8 * (lane >> 4)));
+        w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
+      }
+      qf[rs][c] = __builtin_bit_cast(frag8, w);
     }
-    qf[c] = __builtin_bit_cast(frag8, w);
+    // this row attends to tokens < lim (prefill: its own position included; prefix: the
+    // range's end, so a padding chunk B past it is masked)
+    lim[rs] = PREFILL ? base_pos + (qvalid[rs] ? rq[rs] / G : 0) + 1 : 16 * c1;
   }
-  // this row attends to tokens < lim (prefill: its own position included; prefix: the
-  // range's end, so a padding chunk B past it is masked)
-  const int lim = PREFILL ? base_pos + (qvalid ? rq / G : 0) + 1 : 16 * c1;
   // the smallest limit of the wave's rows (rows grow with the query token): steps below
   // it need no mask
-  const int lim_lo = PREFILL ? __builtin_amdgcn_readfirstlane(base_pos + min(row0 + 16 * wv, nrows - 1) / G + 1)
+  const int lim_lo = PREFILL ? __builtin_amdgcn_readfirstlane(base_pos + min(wrow0, nrows - 1) / G + 1)
                              : 16 * c1;
 
-  // m: the row's reference max (log2 domain, scaled); O: unnormalised output rows
-  // 4(l/16) + i, dims 16jj + l%16; Ol: the same rows' denominators, summed on the matrix
-  // cores as P times a ones tile (every column holds the row sum)
-  float m = kNegInf;
-  f32x4_t O[NJ], Ol = {0.0f, 0.0f, 0.0f, 0.0f};
+  // per set: m, the row's reference max (log2 domain, scaled); O, unnormalised output
+  // rows 4(l/16) + i, dims 16jj + l%16; Ol, the same rows' denominators, summed on the
+  // matrix cores as P times a ones tile (every column holds the row sum)
+  float m[RS];
+  f32x4_t O[RS][NJ], Ol[RS];
 #pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) O[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rs = 0; rs < RS; ++rs) {
+    m[rs] = kNegInf;
+    Ol[rs] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) O[rs][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   const frag8 ones = __builtin_bit_cast(frag8, make_uint4(O_::kOne, O_::kOne, O_::kOne, O_::kOne));
 
   const int bs_shift = BS == 32 ? 5 : 4;  // block size 16 or 32
-  auto tile_off = [&](int c) {  // byte offset of chunk c's rows from kc / vc
-    const int tok = 16 * c;
-    const uint32_t blk = (uint32_t)bt[tok >> bs_shift];
-    return (size_t)blk * blk_bytes + (uint32_t)((tok & (BS - 1)) * ROW);
+  // A step's two chunks (clamped to the range's last one): their physical blocks, read
+  // from the table one step before the step's loads are issued (scalar loads, so that
+  // the issue does not wait for them), and their rows' byte offsets from kc / vc.
+  struct Blk {
+    uint32_t a, b;
+  };
+  auto blk_pair = [&](int cA) {
+    return Blk{(uint32_t)bt[(16 * min(cA, c1 - 1)) >> bs_shift], (uint32_t)bt[(16 * min(cA + 1, c1 - 1)) >> bs_shift]};
+  };
+  auto tile_off = [&](int c, uint32_t blk) {
+    return (size_t)blk * blk_bytes + (uint32_t)(((16 * min(c, c1 - 1)) & (BS - 1)) * ROW);
   };
   // Staging: K piece q = tid + NT k (k < KP) is row q / (D/8) (chunk A for rows < 16, B
   // after), 16-byte piece q % (D/8); V stager (gg, dp) = (tid / (D/2), tid % (D/2))
@@ -226,9 +255,9 @@ rows_kernel(const RowsArgs a) {
     uint32_t v[8];
   };
   // Step at chunk cA (chunks cA, cA + 1): live halves read, padding ones read nothing.
-  auto issue = [&](int cA, Stage& st) {
+  auto issue = [&](int cA, Blk bk, Stage& st) {
     const bool la = cA < c1, lb = cA + 1 < c1;
-    const size_t oa = tile_off(min(cA, c1 - 1)), ob = tile_off(min(cA + 1, c1 - 1));
+    const size_t oa = tile_off(cA, bk.a), ob = tile_off(cA + 1, bk.b);
     const __amdgpu_buffer_rsrc_t ka = tile_rsrc(kc + oa, la ? 16 * ROW : 0);
     const __amdgpu_buffer_rsrc_t kb = tile_rsrc(kc + ob, lb ? 16 * ROW : 0);
 #pragma unroll
@@ -280,71 +309,100 @@ rows_kernel(const RowsArgs a) {
     }
   };
   // One step from LDS buffer buf: S^T = K Q^T for chunks A and B, online softmax over
-  // their 32 tokens, O += P V.
+  // their 32 tokens, O += P V, for every row set of the wave.
   auto compute = [&](int buf, int cA) {
     // A = K rows: lane l reads token l%16 of a chunk, dims 32cc + 8(l/16)
-    f32x4_t SA = {0.0f, 0.0f, 0.0f, 0.0f}, SB = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t SA[RS], SB[RS];
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) SA[rs] = SB[rs] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int cc = 0; cc < NKC; ++cc) {
-      const uint4 ka = *(const uint4*)&lds_k[buf][(lane & 15) * KROW + 32 * cc + 8 * (lane >> 4)];
-      const uint4 kb = *(const uint4*)&lds_k[buf][(16 + (lane & 15)) * KROW + 32 * cc + 8 * (lane >> 4)];
-      SA = O_::qk(__builtin_bit_cast(frag8, ka), qf[cc], SA);
-      SB = O_::qk(__builtin_bit_cast(frag8, kb), qf[cc], SB);
-    }
-    float sv[8];  // raw scores
+      const frag8 ka = __builtin_bit_cast(
+          frag8, *(const uint4*)&lds_k[buf][(lane & 15) * KROW + 32 * cc + 8 * (lane >> 4)]);
+      const frag8 kb = __builtin_bit_cast(
+          frag8, *(const uint4*)&lds_k[buf][(16 + (lane & 15)) * KROW + 32 * cc + 8 * (lane >> 4)]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = SA[i];
-      sv[4 + i] = SB[i];
+      for (int rs = 0; rs < RS; ++rs) {
+        SA[rs] = O_::qk(ka, qf[rs][cc], SA[rs]);
+        SB[rs] = O_::qk(kb, qf[rs][cc], SB[rs]);
+      }
     }
+    float sv[RS][8];  // raw scores
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[rs][i] = SA[rs][i];
+        sv[rs][4 + i] = SB[rs][i];
+      }
     if (16 * cA + 32 > lim_lo) {  // a step reaching some row's limit: mask its tokens past it
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ta = 16 * cA + 4 * (lane >> 4) + i;
-        if (ta >= lim) sv[i] = kNegInf;  // causal mask / range end
-        if (ta + 16 >= lim) sv[4 + i] = kNegInf;
-      }
+      for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ta = 16 * cA + 4 * (lane >> 4) + i;
+          if (ta >= lim[rs]) sv[rs][i] = kNegInf;  // causal mask / range end
+          if (ta + 16 >= lim[rs]) sv[rs][4 + i] = kNegInf;
+        }
     }
-    float bm = pf_max(pf_max(pf_max(sv[0], sv[1]), sv[2]), pf_max(pf_max(sv[3], sv[4]), sv[5]));
-    bm = pf_max(pf_max(bm, sv[6]), sv[7]);
     // every row's first step holds a token it attends to (prefix: all of chunk A;
-    // prefill: token 0), so m is finite from the first step on (a later step masked
-    // for the whole row gives bm = -inf, which moves nothing)
-    bm = pf_xor32_max(pf_xor16_max(bm)) * c_l2;
-    // Lazy rescaling: the reference max m moves only when a score exceeds it by more than
-    // kRescaleSlack (and on the first step, m = -inf), so weights 2^(s - m) stay <= 2^8.
-    // (m, l, acc) stay one consistent partial -- l and acc are sums of 2^(s - m) for the
-    // same m -- so the log-sum-exp algebra is unchanged; only the rare rescale remains.
-    const bool move = bm > m + kRescaleSlack;
-    if (__ballot(move) != 0) {
-      const float mn = move ? bm : m;
-      const float alpha = fast_exp2(m - mn);  // 0 on the first step, 1 for rows kept
-      m = mn;
-      // O rows 4(l/16) + i take the factor of row 4(l/16) + i, held by lane 4(l/16) + i
+    // prefill: token 0), so m is finite from the first step on (a later step masked for
+    // the whole row gives bm = -inf, which moves nothing)
+    float bm[RS];
+    bool move[RS], any = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * (lane >> 4) + i);
-        Ol[i] *= ai;
+    for (int rs = 0; rs < RS; ++rs) {
+      const float* v = sv[rs];
+      float x = pf_max(pf_max(pf_max(v[0], v[1]), v[2]), pf_max(pf_max(v[3], v[4]), v[5]));
+      x = pf_max(pf_max(x, v[6]), v[7]);
+      bm[rs] = pf_xor32_max(pf_xor16_max(x)) * c_l2;
+      // Lazy rescaling: the reference max m moves only when a score exceeds it by more
+      // than kRescaleSlack (and on the first step, m = -inf), so weights 2^(s - m) stay
+      // <= 2^8.  (m, l, acc) stay one consistent partial -- l and acc are sums of
+      // 2^(s - m) for the same m -- so the log-sum-exp algebra is unchanged; only the
+      // rare rescale remains (one branch for all sets).
+      move[rs] = bm[rs] > m[rs] + kRescaleSlack;
+      any = any || move[rs];
+    }
+    if (__ballot(any) != 0) {
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) O[jj][i] *= ai;
+      for (int rs = 0; rs < RS; ++rs) {
+        const float mn = move[rs] ? bm[rs] : m[rs];
+        const float alpha = fast_exp2(m[rs] - mn);  // 0 on the first step, 1 for rows kept
+        m[rs] = mn;
+        // O rows 4(l/16) + i take the factor of row 4(l/16) + i, held by lane 4(l/16) + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * (lane >> 4) + i);
+          Ol[rs][i] *= ai;
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) O[rs][jj][i] *= ai;
+        }
       }
     }
-    float p[8];
+    frag8 ahi[RS], alo[RS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], c_l2, -m));
-    uint32_t hw[4], lw[4];
+    for (int rs = 0; rs < RS; ++rs) {
+      float p[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) O_::split2(p[2 * i], p[2 * i + 1], hw[i], lw[i]);
-    const frag8 ahi = __builtin_bit_cast(frag8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    const frag8 alo = __builtin_bit_cast(frag8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-    Ol = O_::qk(ahi, ones, Ol);
-    Ol = O_::qk(alo, ones, Ol);
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[rs][i], c_l2, -m[rs]));
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O_::split2(p[2 * i], p[2 * i + 1], hw[i], lw[i]);
+      ahi[rs] = __builtin_bit_cast(frag8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      alo[rs] = __builtin_bit_cast(frag8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      Ol[rs] = O_::qk(ahi[rs], ones, Ol[rs]);
+      Ol[rs] = O_::qk(alo[rs], ones, Ol[rs]);
+    }
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
-      const uint4 vv = *(const uint4*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 8];
-      const frag8 vf = __builtin_bit_cast(frag8, vv);
-      O[jj] = O_::qk(ahi, vf, O[jj]);
-      O[jj] = O_::qk(alo, vf, O[jj]);
+      const frag8 vf = __builtin_bit_cast(
+          frag8, *(const uint4*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 8]);
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) {
+        O[rs][jj] = O_::qk(ahi[rs], vf, O[rs][jj]);
+        O[rs][jj] = O_::qk(alo[rs], vf, O[rs][jj]);
+      }
     }
   };
 
@@ -359,7 +417,8 @@ rows_kernel(const RowsArgs a) {
     const int n = (c1 - c0 + 1) / 2;  // steps
     Stage ring[PD];
 #pragma unroll
-    for (int u = 0; u < PD; ++u) issue(c0 + 2 * u, ring[u]);
+    for (int u = 0; u < PD; ++u) issue(c0 + 2 * u, blk_pair(c0 + 2 * u), ring[u]);
+    Blk next = blk_pair(c0 + 2 * PD);  // the blocks of the next step issued
     stage(0, c0, ring[0]);
     __syncthreads();
     for (int i = 0; i < n; i += PD) {
@@ -367,42 +426,51 @@ rows_kernel(const RowsArgs a) {
       for (int u = 0; u < PD; ++u) {
         const int ii = i + u;
         if (ii >= n) break;
-        issue(c0 + 2 * (ii + PD), ring[u]);
+        issue(c0 + 2 * (ii + PD), next, ring[u]);
         compute(ii & 1, c0 + 2 * ii);
         if (ii + 1 < n) stage((ii + 1) & 1, c0 + 2 * (ii + 1), ring[(u + 1) % PD]);
+        // the next issue's blocks: scalar loads placed before the barrier, whose wait
+        // for the step's LDS writes covers them too
+        next = blk_pair(c0 + 2 * (ii + PD + 1));
         __syncthreads();
       }
     }
   }
 
   if constexpr (PREFILL) {
-    // ---- output rows 4(l/16) + i, dims 16jj + l%16: acc / l of that row, rounded to
-    // the output dtype
+    // ---- output rows 4(l/16) + i of each set, dims 16jj + l%16: acc / l of that row,
+    // rounded to the output dtype
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float li = Ol[i];
-      const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
-      if (rr >= nrows) continue;
-      const float inv = li != 0.0f ? 1.0f / li : 0.0f;
-      const size_t o = ((size_t)(qbase + rr / G) * a.num_q_heads + g * G + rr % G) * D + (lane & 15);
+    for (int rs = 0; rs < RS; ++rs) {
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) store_out(a.out, o + 16 * jj, a.out_dtype, O[jj][i] * inv);
+      for (int i = 0; i < 4; ++i) {
+        const float li = Ol[rs][i];
+        const int rr = wrow0 + 16 * rs + 4 * (lane >> 4) + i;
+        if (rr >= nrows) continue;
+        const float inv = li != 0.0f ? 1.0f / li : 0.0f;
+        const size_t o = ((size_t)(qbase + rr / G) * a.num_q_heads + g * G + rr % G) * D + (lane & 15);
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) store_out(a.out, o + 16 * jj, a.out_dtype, O[rs][jj][i] * inv);
+      }
     }
   } else {
-    // ---- partials: m per row (lanes 0..15: row l%16), l and acc of rows 4(l/16) + i
-    // (l from the lanes of column 0), acc dims 16jj + l%16
+    // ---- partials: m per row (lanes 0..15: row l%16 of the set), l and acc of rows
+    // 4(l/16) + i (l from the lanes of column 0), acc dims 16jj + l%16
     auto part_of = [&](int rr) {
       return a.pre_part + (((size_t)(qbase + rr / G) * a.num_q_heads + g * G + rr % G) * T + t) * STRIDE;
     };
-    if (lane < 16 && qvalid) part_of(rq)[0] = m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = row0 + 16 * wv + 4 * (lane >> 4) + i;
-      if (rr >= nrows) continue;
-      float* pp = part_of(rr);
-      if ((lane & 15) == 0) pp[1] = Ol[i];
+    for (int rs = 0; rs < RS; ++rs) {
+      if (lane < 16 && qvalid[rs]) part_of(rq[rs])[0] = m[rs];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) pp[4 + 16 * jj + (lane & 15)] = O[jj][i];
+      for (int i = 0; i < 4; ++i) {
+        const int rr = wrow0 + 16 * rs + 4 * (lane >> 4) + i;
+        if (rr >= nrows) continue;
+        float* pp = part_of(rr);
+        if ((lane & 15) == 0) pp[1] = Ol[rs][i];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) pp[4 + 16 * jj + (lane & 15)] = O[rs][jj][i];
+      }
     }
   }
 }

@@ -78,7 +78,7 @@ struct RowsArgs {
   void* out;                    // [rows][H_q][D]
   int out_dtype;
 };
-constexpr int kPrefixRows = 64;  // query rows per workgroup of the rows kernel
+constexpr int kPrefixRows = 128;  // query rows per workgroup of the rows kernel
 hipError_t launch_prefix(const RowsArgs& a, int num_groups);
 hipError_t launch_prefill(const RowsArgs& a);
 
