@@ -59,6 +59,8 @@ def parse_args():
                     help="prefix-sharing workloads: plain decode instead of the shared-prefix entry point")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy --steps times (counter calibration)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the chunked-prefill leg (--reps calls) and print its result")
     return ap.parse_args()
 
 
@@ -477,6 +479,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.steps} x {src.numel() * 4} bytes")
+        return
+    if args.prefill_only:
+        print(json.dumps(measure_prefill(args)))
         return
     cfg = pick_config(args.config)
     w, st, res = measure(cfg, args)

@@ -126,13 +126,13 @@ int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
   if (pkv::streamk_plan(c->dtype, q_dtype, c->head_dim, G, num_seqs, true, true, &out->sk) != 0)
     return PKV_ERR_SHAPE;
   out->tiles = (int32_t)(((int64_t)max_group_size * G + pkv::kPrefixRows - 1) / pkv::kPrefixRows);
-  // Enough prefix workgroups (4 waves each) for one per CU (the suffix pass runs one
+  // Enough prefix workgroups (4 waves each) for two per CU (the suffix pass runs one
   // workgroup of sk.waves / CUs = 8 waves per CU), at most 8 slices and at most one per
   // 16-token chunk of the longest prefix.  (Every slice adds a partial per row that the
   // suffix pass folds in: on the 256-sequence workload 4 slices measured faster than 8
   // and than 2.)
   const int64_t per_split = (int64_t)num_groups * out->tiles * c->num_kv_heads;
-  const int64_t wgs = out->sk.waves / 8 > 0 ? out->sk.waves / 8 : 1;
+  const int64_t wgs = out->sk.waves / 4 > 0 ? out->sk.waves / 4 : 1;
   int64_t splits = (wgs + per_split - 1) / per_split;
   const int64_t max_splits = max_prefix_len / 16 > 0 ? max_prefix_len / 16 : 1;
   splits = splits < 1 ? 1 : (splits > 8 ? 8 : splits);
@@ -486,7 +486,7 @@ int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, 
   if (!q || !cu_q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
   const int32_t G = num_q_heads / cache->num_kv_heads;
-  const int64_t tiles = ((int64_t)max_q_len * G + pkv::kPrefixRows - 1) / pkv::kPrefixRows;
+  const int64_t tiles = ((int64_t)max_q_len * G + pkv::kPrefillRows - 1) / pkv::kPrefillRows;
   if (tiles * num_seqs * cache->num_kv_heads > 0x7fffffff) return PKV_ERR_SHAPE;
   pkv::RowsArgs p = rows_args(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
                               max_blocks_per_seq, scale, (int32_t)tiles, stream);

@@ -97,13 +97,20 @@ __device__ __forceinline__ float pf_xor32_max(float x) {
 }
 
 constexpr int kRowsWaves = 4;
-// Each wave owns kRowSets sets of 16 query rows: one step's K and V fragments, read once
-// from LDS, feed the MFMAs of every set, and the sets' softmax chains are independent.
-constexpr int kRowSets = kPrefixRows / (16 * kRowsWaves);
+// Each wave owns RowSets<PREFILL> sets of 16 query rows: one step's K and V fragments,
+// read once from LDS, feed the MFMAs of every set, and the sets' softmax chains are
+// independent.  Chunked prefill (long ranges, many rows) takes two sets: ~170 VGPRs, two
+// waves per SIMD.  The shared-prefix pass (a few 64-row tiles per KV head, short slices)
+// keeps one set at <= 128 VGPRs and four waves per SIMD, which measured ~3 us faster on
+// the 256-sequence workload than two sets.
+template <bool PREFILL> struct RowSets {
+  static constexpr int n = PREFILL ? 2 : 1;
+  static constexpr int rows = 16 * kRowsWaves * n;  // query rows per workgroup
+  static constexpr int waves_per_simd = PREFILL ? 2 : 4;
+};
+static_assert(RowSets<true>::rows == kPrefillRows && RowSets<false>::rows == kPrefixRows,
+              "row tiles agree with the host plan");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay <= 2^8 between rescales
-// Two workgroups of four waves per CU (two waves per SIMD, <= 256 VGPRs each): a
-// workgroup waits at its per-step barrier while the other computes.
-constexpr int kRowsWavesPerSimd = 2;
 constexpr int kRowsDepth = 1;  // steps (32 tokens each) whose loads are in flight
 
 // PREFILL = false: shared-prefix partials; true: causal chunked prefill.
@@ -114,7 +121,8 @@ constexpr int kRowsDepth = 1;  // steps (32 tokens each) whose loads are in flig
 // 16x16x32 P.V MFMA (the contraction order is free as long as V uses the same one), so
 // V is staged as [lane group g][dim][tokens 4g..4g+3 of A, 4g..4g+3 of B].
 template <int KV, int D, bool PREFILL>
-__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(kRowsWavesPerSimd)))
+__global__ void __launch_bounds__(64 * kRowsWaves)
+    __attribute__((amdgpu_waves_per_eu(RowSets<PREFILL>::waves_per_simd)))
 rows_kernel(const RowsArgs a) {
   using O_ = PfxOps<KV>;
   using frag8 = typename O_::frag8;
@@ -142,7 +150,7 @@ rows_kernel(const RowsArgs a) {
   int T = 1, t = 0, s, nrows, c0, c1, qbase, row0, base_pos = 0, ctx = 0;
   if constexpr (PREFILL) {
     // rows (query token i, head) of sequence s: row r -> token r / G, head g G + r % G
-    row0 = (bid % a.tiles) * kPrefixRows;
+    row0 = (bid % a.tiles) * kPrefillRows;
     s = bid / a.tiles;
     const int n = a.cu_q[s + 1] - a.cu_q[s];
     nrows = n * G;
@@ -150,7 +158,7 @@ rows_kernel(const RowsArgs a) {
     ctx = a.context_lens[s];
     base_pos = ctx - n;         // position of query token 0
     qbase = a.cu_q[s];
-    const int last = min(nrows, row0 + kPrefixRows) - 1;
+    const int last = min(nrows, row0 + kPrefillRows) - 1;
     c0 = 0;
     c1 = (base_pos + last / G + 1 + 15) / 16;  // through the last row's own token
   } else {
@@ -187,7 +195,7 @@ rows_kernel(const RowsArgs a) {
 
   // ---- this lane's query row in each set rs (B operand of S^T = K Q^T: row l%16 of the
   // set, dims 8(l/16) + 32c); the wave's rows are row0 + 16 (RS wv + rs) + 0..15
-  constexpr int RS = kRowSets;
+  constexpr int RS = RowSets<PREFILL>::n;
   const int wrow0 = row0 + 16 * RS * wv;
   int rq[RS], lim[RS];
   bool qvalid[RS];

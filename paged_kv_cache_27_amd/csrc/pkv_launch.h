@@ -65,7 +65,7 @@ struct RowsArgs {
   const int32_t* block_tables;
   int32_t max_blocks_per_seq;
   float scale;
-  int32_t tiles;                // kPrefixRows-row tiles per group / per sequence
+  int32_t tiles;                // kPrefixRows-row tiles per group / kPrefillRows-row tiles per sequence
   hipStream_t stream;
   // shared prefix
   const int32_t* group_starts;  // [groups + 1]
@@ -78,7 +78,8 @@ struct RowsArgs {
   void* out;                    // [rows][H_q][D]
   int out_dtype;
 };
-constexpr int kPrefixRows = 128;  // query rows per workgroup of the rows kernel
+constexpr int kPrefixRows = 64;    // query rows per workgroup of the rows kernel: shared-prefix pass
+constexpr int kPrefillRows = 128;  // the same for chunked prefill
 hipError_t launch_prefix(const RowsArgs& a, int num_groups);
 hipError_t launch_prefill(const RowsArgs& a);
 
