@@ -183,3 +183,49 @@ def test_shared_prefix_argument_errors():
     assert _prefix_call(lib, _desc(), n=0) == 0
     assert pkv.paged_attention_shared_prefix_workspace_size(_desc(dtype=pkv.FP8_E4M3), pkv.BF16,
                                                             4, 4, 100, 1, 4, 32) == 0
+
+
+def _prefill_call(lib, desc, q_dtype=pkv.BF16, n=2, hq=4, cu=FAKE, maxq=16, maxb=4, maxctx=40,
+                  out_dtype=pkv.BF16, q=FAKE, out=FAKE):
+    return lib.paged_attention_prefill(q, q_dtype, n, hq, cu, maxq, FAKE, FAKE, ctypes.byref(desc), FAKE,
+                                       maxb, FAKE, maxctx, 0.1, out, out_dtype, None)
+
+
+def test_prefill_argument_errors():
+    lib = pkv.load_library()
+    assert _prefill_call(lib, _desc(dtype=pkv.FP8_E4M3)) == -2  # 16-bit caches only
+    assert _prefill_call(lib, _desc(dtype=pkv.F32), q_dtype=pkv.F32) == -2
+    assert _prefill_call(lib, _desc(), q_dtype=pkv.F16) == -2  # q dtype != cache dtype
+    assert _prefill_call(lib, _desc(), out_dtype=pkv.FP8_E4M3) == -2
+    assert _prefill_call(lib, _desc(head_dim=96)) == -3
+    assert _prefill_call(lib, _desc(), hq=5) == -4
+    assert _prefill_call(lib, _desc(num_kv_heads=1), hq=17) == -3  # group of 17
+    assert _prefill_call(lib, _desc(), maxq=41) == -3  # a chunk longer than the longest context
+    assert _prefill_call(lib, _desc(), maxq=-1) == -3
+    assert _prefill_call(lib, _desc(), maxb=2) == -3  # table too short for max_context_len
+    assert _prefill_call(lib, _desc(), cu=None) == -1
+    assert _prefill_call(lib, _desc(), q=None) == -1
+    assert _prefill_call(lib, _desc(), out=None) == -1
+    assert _prefill_call(lib, _desc(), q=ctypes.c_void_p(0x100004)) == -3  # misaligned
+    assert _prefill_call(lib, _desc(), n=0) == 0  # nothing to do
+    assert _prefill_call(lib, _desc(), maxq=0) == 0
+
+
+def test_block_move_argument_errors():
+    lib = pkv.load_library()
+    d = ctypes.byref(_desc())
+    mis = ctypes.c_void_p(0x100004)
+    copy, out, into = lib.paged_kv_copy_blocks, lib.paged_kv_swap_out, lib.paged_kv_swap_in
+    assert copy(FAKE, FAKE, -1, FAKE, FAKE, d, None) == -3
+    assert copy(None, None, 0, None, None, d, None) == 0  # nothing to move
+    assert copy(None, FAKE, 3, FAKE, FAKE, d, None) == -1
+    assert copy(FAKE, FAKE, 3, FAKE, FAKE, None, None) == -1
+    assert copy(FAKE, FAKE, 3, mis, FAKE, d, None) == -3
+    assert copy(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(_desc(dtype=7)), None) == -2
+    assert copy(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(_desc(block_size=8)), None) == -3
+    for f, args in ((out, lambda n, buf: (FAKE, n, FAKE, FAKE, d, buf, FAKE, None)),
+                    (into, lambda n, buf: (FAKE, n, buf, FAKE, FAKE, FAKE, d, None))):
+        assert f(*args(-1, FAKE)) == -3
+        assert f(*args(0, None)) == 0
+        assert f(*args(2, None)) == -1
+        assert f(*args(2, mis)) == -3  # buffers 16-byte aligned
