@@ -253,6 +253,69 @@ def traffic_for(cfg_name):
     return entry.get("bytes_per_call")
 
 
+def decode_tiles(w):
+    """The 16-token K/V tiles a decode reads, as indices in units of tile bytes into each
+    cache, in the balanced schedule's order (KV head, then sequence, then chunk); only
+    attended chunks under a window; a tile shared by several sequences (a shared prefix)
+    listed once, where it is first met (the bytes HBM must deliver)."""
+    import numpy as np
+    c = w.cfg
+    B, hkv = c.block_size, c.num_kv_heads
+    per_head = []
+    for s in range(c.num_seqs):
+        ctx = int(w.context_lens[s])
+        if ctx == 0:
+            continue
+        chunks = np.unique(window_tokens(ctx, c.window, c.sinks) // 16)
+        blk = w.block_tables[s][(16 * chunks) // B].astype(np.int64)
+        per_head.append(blk * B + (16 * chunks) % B)  # rows of head 0, in units of token rows
+    rows = np.concatenate(per_head)
+    out = []
+    for g in range(hkv):
+        t = ((rows // B) * hkv + g) * B + rows % B
+        _, first = np.unique(t, return_index=True)
+        out.append(t[np.sort(first)] // 16)
+    return np.concatenate(out).astype(np.int32)
+
+
+def read_ceiling(w, st, reps):
+    """Achievable read rate of the decode's K/V access pattern: the streaming-read probe
+    (libpkv_probe.so, loads as the decode kernel issues them, no arithmetic) over
+    decode_tiles(w), L2/MALL flushed before each rep, HIP events on the current stream."""
+    import ctypes
+    import numpy as np
+    import torch
+    from paged_kv_cache_27_amd._binding import LIB_PATH
+
+    lib = ctypes.CDLL(str(Path(LIB_PATH).with_name("libpkv_probe.so")))
+    f = lib.pkv_probe_read_tiles
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    c = w.cfg
+    tb = 16 * c.head_dim * DT_BYTES[c.kv_dtype]
+    tiles = torch.from_numpy(decode_tiles(w)).cuda()
+    n = tiles.numel()
+    assert int(tiles.max()) < st.k_cache.numel() * st.k_cache.element_size() // tb
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lambda: f(st.k_cache.data_ptr(), st.v_cache.data_ptr(), tiles.data_ptr(), n, tb, sink.data_ptr(),
+                     stream)
+    assert call() == 0
+    flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    fsink = torch.empty((), dtype=torch.float32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        fsink.copy_(flush.sum())
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return {"kernel": "pkv_probe_read_tiles", "tiles": n, "tile_bytes": tb, "bytes": 2 * n * tb,
+            "ms_cold_mean": ms, "GBps": 2 * n * tb / (ms * 1e-3) / 1e9}
+
+
 def measure(cfg, args, partition=None):
     import numpy as np
     import torch
@@ -311,9 +374,16 @@ def measure(cfg, args, partition=None):
         "bytes": nbytes, "schedule": st.schedule,
         "max_context_len": w.max_context_len, "sum_context": int(w.context_lens.sum()),
     }
+    ceil = read_ceiling(w, st, args.reps)
+    # the same tiles read by the probe alone vs by the decode (which also reads q and the
+    # tables and computes): the decode's fraction of the pattern's achievable rate
+    ceil["decode_frac"] = ceil["ms_cold_mean"] / dec_ms
+    res["read_ceiling"] = ceil
     log(f"[{cfg.name}] step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s), decode cold "
         f"{dec_ms * 1e3:.1f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak), "
-        f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, schedule {res['schedule']}")
+        f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, schedule {res['schedule']}; read ceiling of its "
+        f"tiles {ceil['GBps']:.0f} GB/s ({ceil['ms_cold_mean'] * 1e3:.1f} us), decode at "
+        f"{100 * ceil['decode_frac']:.1f}% of it")
     return w, st, res
 
 
@@ -524,6 +594,8 @@ def main():
                      "bytes_per_launch": res["bytes"]["decode"],
                      "mean_launch_ms": round(res["decode_ms_cold_mean"], 6)},
         "cpu_baseline": cpu,
+        "read_ceiling": {k: (round(v, 4) if isinstance(v, float) else v)
+                         for k, v in res["read_ceiling"].items()},
     }
     if args.json_out:
         Path(args.json_out).parent.mkdir(parents=True, exist_ok=True)

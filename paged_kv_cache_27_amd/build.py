@@ -1,7 +1,8 @@
 """Build the HIP library (libpagedkv.so) in-tree for gfx950 with hipcc.
 
 `python -m paged_kv_cache_27_amd.build` compiles every source under csrc/ to an
-object in _build/ (in parallel) and links the shared library next to this file.
+object in _build/ (in parallel) and links the shared library next to this file; the
+measurement-only streaming-read probe (probe/) becomes libpkv_probe.so beside it.
 """
 from __future__ import annotations
 
@@ -16,6 +17,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libpagedkv.so"
+PROBE_SRC = PKG / "probe" / "probe_read.hip"
+PROBE_LIB = PKG / "libpkv_probe.so"
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -45,15 +48,18 @@ def _compile(src: Path) -> Path:
 def build(verbose: bool = True) -> Path:
     BUILD.mkdir(exist_ok=True)
     sources = sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
-    jobs = min(len(sources), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
+    jobs = min(len(sources) + 1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
     with cf.ThreadPoolExecutor(max_workers=max(jobs, 1)) as ex:
+        probe = ex.submit(_compile, PROBE_SRC)
         objs = list(ex.map(_compile, sources))
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+        probe_obj = probe.result()
+    for lib, parts in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+        tmp = lib.with_suffix(".so.tmp")
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, parts), "-o", str(tmp)]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB.name}")
     return LIB
 
 

@@ -197,7 +197,7 @@ struct ValuDecoder {
   const uint8_t* kc;
   const uint8_t* vc;
   const int32_t* bt;
-  int BS, Hkv, G, g, tok_end;
+  int BS, bs_shift, Hkv, G, g, tok_end;
   int win_lo, sink_hi;  // attended: tokens >= win_lo or < sink_hi (and < tok_end)
 
   __device__ __forceinline__ void init(const DecodeArgs& a, float* p_tile, float* alpha_tile) {
@@ -210,6 +210,7 @@ struct ValuDecoder {
     kc = (const uint8_t*)a.k_cache;
     vc = (const uint8_t*)a.v_cache;
     BS = a.block_size;
+    bs_shift = BS == 32 ? 5 : 4;  // the host admits block sizes 16 and 32
     Hkv = a.num_kv_heads;
     G = a.num_q_heads / a.num_kv_heads;
   }
@@ -245,7 +246,7 @@ struct ValuDecoder {
   // Physical block of chunk c (tokens 16c ..), a scalar load: the index is uniform,
   // and the scalar path keeps table reads out of the vector-memory counter.
   __device__ __forceinline__ int table_entry(int c) const {
-    const int idx = __builtin_amdgcn_readfirstlane((16 * c) / BS);
+    const int idx = __builtin_amdgcn_readfirstlane(16 * c) >> bs_shift;
     const uint64_t p = (uint64_t)(uintptr_t)bt;
     const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
@@ -254,8 +255,10 @@ struct ValuDecoder {
 
   // live == false: a padding step past the range's end; its loads read nothing.
   __device__ __forceinline__ void load_chunk(int ct, int blk, R& buf, bool live) {
-    const int lb = ct / BS;
-    const size_t tile = (((size_t)blk * Hkv + g) * BS + (ct - lb * BS)) * ROW;
+    // scalar: the chunk, its block and the head are wave-uniform (block size 16 or 32)
+    const uint32_t row = (uint32_t)(__builtin_amdgcn_readfirstlane(ct) & (BS - 1));
+    const size_t tile = (((size_t)(uint32_t)__builtin_amdgcn_readfirstlane(blk) * (uint32_t)Hkv +
+                          (uint32_t)__builtin_amdgcn_readfirstlane(g)) * (uint32_t)BS + row) * ROW;
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + tile, live ? 16 * ROW : 0);
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + tile, live ? 16 * ROW : 0);
 #pragma unroll
@@ -468,9 +471,11 @@ struct MfmaDecoder {
   using T = Qk<KV, Q>;
   using P = Pv<KV>;
   using Buf = MfmaChunk<KV, D>;
-  // Chunks whose loads are in flight ahead of the one computed.  An fp8 chunk is half
-  // the bytes of a 16-bit one, so it keeps three ahead to hold as many bytes in flight.
-  static constexpr int kDepth = KV == kFP8 ? 3 : 1;
+  // Chunks whose loads are in flight ahead of the one computed: one for 16-bit caches,
+  // two for fp8 (half the bytes per chunk).  (Three for fp8 -- as many bytes in flight as
+  // the 16-bit decoder -- measured 12 % slower on the 70B-shaped workload, and
+  // pushed its 8-head decoder past 256 VGPRs.)
+  static constexpr int kDepth = KV == kFP8 ? 2 : 1;
   static constexpr int EB = DtInfo<KV>::bytes;
   static constexpr int ROW = Buf::ROW, NC = Buf::NC, VW = Buf::VW, VBYTES = Buf::VBYTES;
   static constexpr int QB = DtInfo<Q>::bytes;
@@ -485,7 +490,7 @@ struct MfmaDecoder {
   const uint8_t* kc;
   const uint8_t* vc;
   const int32_t* bt;
-  int BS, Hkv, G, g, tok_end;
+  int BS, bs_shift, Hkv, G, g, tok_end;
   int win_lo, sink_hi;  // attended: tokens >= win_lo or < sink_hi (and < tok_end)
 
   __device__ __forceinline__ void init(const DecodeArgs& a, float*, float*) {
@@ -495,6 +500,7 @@ struct MfmaDecoder {
     kc = (const uint8_t*)a.k_cache;
     vc = (const uint8_t*)a.v_cache;
     BS = a.block_size;
+    bs_shift = BS == 32 ? 5 : 4;  // the host admits block sizes 16 and 32
     Hkv = a.num_kv_heads;
     G = a.num_q_heads / a.num_kv_heads;
   }
@@ -527,19 +533,28 @@ struct MfmaDecoder {
   __device__ __forceinline__ bool keep(int t) const { return t < tok_end && (t >= win_lo || t < sink_hi); }
 
   __device__ __forceinline__ int table_entry(int c) const {
-    const int idx = __builtin_amdgcn_readfirstlane((16 * c) / BS);
+    const int idx = __builtin_amdgcn_readfirstlane(16 * c) >> bs_shift;
     const uint64_t p = (uint64_t)(uintptr_t)bt;
     const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
     return ((const __attribute__((address_space(4))) int32_t*)pu)[idx];
   }
 
-  // live == false: a padding step past the range's end; its loads read nothing.
+  // live == false: a padding step past the range's end; its loads read nothing.  The
+  // resources cover only the chunk's rows before the context's end, so the rows past it
+  // (the tail of the last block: any bytes, NaN included) load as zeros: their scores
+  // are masked and their zero V rows cannot spoil the P.V products.  Rows outside a
+  // window but inside a chunk that holds attended tokens are tokens written earlier,
+  // in a block that is still live: only their scores need masking.
   __device__ __forceinline__ void load_chunk(int ct, int blk, Buf& buf, bool live) {
-    const int lb = ct / BS;
-    const size_t tile = (((size_t)blk * Hkv + g) * BS + (ct - lb * BS)) * ROW;
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + tile, live ? 16 * ROW : 0);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + tile, live ? 16 * ROW : 0);
+    // scalar: the chunk, its block and the head are wave-uniform (block size 16 or 32)
+    const int ctu = __builtin_amdgcn_readfirstlane(ct);
+    const uint32_t row = (uint32_t)(ctu & (BS - 1));
+    const size_t tile = (((size_t)(uint32_t)__builtin_amdgcn_readfirstlane(blk) * (uint32_t)Hkv +
+                          (uint32_t)__builtin_amdgcn_readfirstlane(g)) * (uint32_t)BS + row) * ROW;
+    const int rows = live ? min(16, __builtin_amdgcn_readfirstlane(tok_end) - ctu) : 0;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + tile, rows * ROW);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + tile, rows * ROW);
     const int krow = 4 * (lane & 3) + ((lane & 15) >> 2);  // A-operand row l%16 -> token
 #pragma unroll
     for (int c2 = 0; c2 < NC; ++c2)
@@ -573,16 +588,6 @@ struct MfmaDecoder {
         for (int hs = 0; hs < HS; ++hs) S[hs] = T::mma(kf, qf[hs][c2 * T::SUB + j], S[hs]);
       }
     const int tb = ct + (lane >> 4);
-    if (ct + 16 > tok_end || ct < win_lo) {
-      // last chunk of the context, or a chunk only partly attended: rows not attended
-      // are never let in (their bytes may be anything, NaN included)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (!keep(tb + 4 * k)) {
-#pragma unroll
-          for (int w = 0; w < VW; ++w) buf.v[k][w] = 0u;
-        }
-    }
     // ---- online softmax, one head per lane (duplicated over lane & 3)
     float p[HS][4], alpha[HS];
     bool changed = false;
@@ -711,6 +716,14 @@ template <class W>
 __device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int step, int split = 0x7fffffff,
                                            int shift = 0) {
   constexpr int DEPTH = W::kDepth;
+  // wave-uniform by construction; said so, so that the chunk and address arithmetic stays
+  // scalar (in vector registers it had competed with the in-flight loads for registers,
+  // and the compiler then drained every load at the top of the loop)
+  c_begin = __builtin_amdgcn_readfirstlane(c_begin);
+  c_end = __builtin_amdgcn_readfirstlane(c_end);
+  step = __builtin_amdgcn_readfirstlane(step);
+  split = __builtin_amdgcn_readfirstlane(split);
+  shift = __builtin_amdgcn_readfirstlane(shift);
   if (c_begin >= c_end) return;
   const int n = (c_end - c_begin + step - 1) / step;  // chunks of this wave
   auto chunk = [&](int i) {
@@ -724,16 +737,22 @@ __device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int st
     wd.load_chunk(16 * chunk(j), blk, buf[j], j < n);
     blk = wd.table_entry(chunk(j + 1));
   }
-  for (int i = 0; i < n; i += DEPTH + 1) {
+  // Whole rounds of DEPTH + 1 chunks, with no exit inside a round (an exit there made
+  // the compiler copy the in-flight buffers at the loop edge and wait for their loads),
+  // then the last n mod (DEPTH + 1) chunks, already loaded in buf[0 ..].
+  const int full = n - n % (DEPTH + 1);
+  for (int i = 0; i < full; i += DEPTH + 1) {
 #pragma unroll
     for (int u = 0; u <= DEPTH; ++u) {
       const int ii = i + u;
-      if (ii >= n) break;
       wd.load_chunk(16 * chunk(ii + DEPTH), blk, buf[(u + DEPTH) % (DEPTH + 1)], ii + DEPTH < n);
       blk = wd.table_entry(chunk(ii + DEPTH + 1));
       wd.process_chunk(16 * chunk(ii), buf[u]);
     }
   }
+#pragma unroll
+  for (int u = 0; u < DEPTH; ++u)
+    if (full + u < n) wd.process_chunk(16 * chunk(full + u), buf[u]);
 }
 
 // Log-sum-exp merge of P partial results of one query head (the online-softmax

@@ -229,3 +229,24 @@ def test_block_move_argument_errors():
         assert f(*args(0, None)) == 0
         assert f(*args(2, None)) == -1
         assert f(*args(2, mis)) == -3  # buffers 16-byte aligned
+
+
+def _probe():
+    lib = ctypes.CDLL(str(Path(pkv.load_library()._name).with_name("libpkv_probe.so")))
+    f = lib.pkv_probe_read_tiles
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    return f
+
+
+def test_probe_library_argument_errors():
+    """The measurement-only streaming-read probe (include/pkv_probe.h) loads beside the
+    library and rejects bad arguments before touching a device."""
+    f = _probe()
+    assert f(FAKE, FAKE, FAKE, -1, 4096, FAKE, None) == -3
+    assert f(None, None, None, 0, 4096, None, None) == 0  # nothing to read
+    assert f(None, FAKE, FAKE, 5, 4096, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, 5, 4096, None, None) == -1
+    assert f(FAKE, FAKE, FAKE, 5, 3000, FAKE, None) == -3  # unsupported tile size
+    assert f(ctypes.c_void_p(0x100004), FAKE, FAKE, 5, 4096, FAKE, None) == -3
