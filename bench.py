@@ -488,8 +488,9 @@ def measure_prefill(args):
 
 
 def cpu_baseline(w, budget_s):
-    """The fp64 oracle on this host's cores over whole sequences (all query heads), taken
-    in order until the wall budget is spent."""
+    """The fp64 oracle on this host's cores (up to 16 threads) over whole sequences (all
+    query heads), taken in order until the wall budget is spent; then the same on one
+    thread for a third of the budget (`single_thread`)."""
     import numpy as np
     from oracle.oracle import Oracle
     from workloads import poisoned_cache
@@ -502,8 +503,18 @@ def cpu_baseline(w, budget_s):
     ns = orc.slot_mapping(w.new_seq, w.new_pos, w.block_tables, c.block_size)
     orc.kv_write(ns, w.new_k, w.new_v, c.src_dtype, kc, vc, c.kv_dtype, w.k_scale, w.v_scale)
     threads = min(16, len(os.sched_getaffinity(0)))
-    # Whole passes over the workload (all sequences, all query heads) until the budget is
-    # spent; the last pass may stop early at a sequence boundary.
+    res = _oracle_rate(orc, w, kc, vc, threads, budget_s)
+    one = _oracle_rate(orc, w, kc, vc, 1, budget_s / 3)
+    res["single_thread"] = {"value": one["value"], "unit": "GB/s", "cores": 1, "sample": one["sample"]}
+    return res
+
+
+def _oracle_rate(orc, w, kc, vc, threads, budget_s):
+    """Whole passes of the oracle's decode over the workload (all sequences, all query
+    heads) on `threads` threads until the budget is spent; the last pass may stop early
+    at a sequence boundary."""
+    import numpy as np
+    c = w.cfg
     passes, elapsed, tokens, seq_heads = 0, 0.0, 0, 0
     per = max(1, threads // 2)
     while elapsed < budget_s:
@@ -528,6 +539,19 @@ def cpu_baseline(w, budget_s):
                       f"{elapsed:.1f}s wall on {threads} threads"}
 
 
+def gpu_clocks():
+    """Current clocks as rocm-smi reports them (a child process, started before this
+    process touches the GPU), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except Exception:  # tool missing or stuck: the record just goes without clocks
+        return None
+    lines = [(ln.split(":", 1)[1] if ln.lstrip().startswith("GPU[") else ln).strip()
+             for ln in r.stdout.splitlines() if any(x in ln for x in ("sclk", "mclk", "fclk"))]
+    return "; ".join(lines[:6]) or None
+
+
 def main():
     args = parse_args()
     args.reps = max(1, args.reps)
@@ -536,12 +560,16 @@ def main():
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this path has "
               "no multi-GPU leg; sharding is described in DESIGN.md", file=sys.stderr)
         sys.exit(2)
+    clocks = gpu_clocks() if not args.copy_calibration and not args.prefill_only else None
     import torch
     import paged_kv_cache_27_amd as pkv
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     pkv.load_library()  # raises if the HIP library is missing: there is no fallback
+    props = torch.cuda.get_device_properties(0)
+    env = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+           "clocks": clocks, "torch": torch.__version__, "hip": torch.version.hip}
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -571,7 +599,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
-        log(f"[cpu oracle] {cpu['value']:.3f} GB/s on {cpu['cores']} threads: {cpu['sample']}")
+        log(f"[cpu oracle] {cpu['value']:.3f} GB/s on {cpu['cores']} threads: {cpu['sample']}; "
+            f"{cpu['single_thread']['value']:.3f} GB/s on one thread")
     traffic = traffic_for(cfg.name)
     c = cfg
     line = {
@@ -596,6 +625,7 @@ def main():
         "cpu_baseline": cpu,
         "read_ceiling": {k: (round(v, 4) if isinstance(v, float) else v)
                          for k, v in res["read_ceiling"].items()},
+        "env": env,
     }
     if args.json_out:
         Path(args.json_out).parent.mkdir(parents=True, exist_ok=True)
