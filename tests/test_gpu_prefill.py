@@ -24,7 +24,7 @@ def _gpu():
     pkv.load_library()
 
 
-def _run(orc, cfg, chunk_lens, seed=77, scale=None):
+def _run(orc, cfg, chunk_lens, seed=77, scale=None, max_q_len=None):
     w = make_workload(cfg)
     if scale is not None:
         w = dataclasses.replace(w, scale=scale)
@@ -34,7 +34,8 @@ def _run(orc, cfg, chunk_lens, seed=77, scale=None):
     c = w.cfg
     q, cu = prefill_queries(w, chunk_lens, seed)
     out = torch.empty((int(cu[-1]), c.num_q_heads, c.head_dim), dtype=torch_dtype(c.out_dtype), device="cuda")
-    pkv.paged_attention_prefill(to_device(q, c.q_dtype), torch.from_numpy(cu).cuda(), int(np.max(chunk_lens)),
+    mq = int(np.max(chunk_lens)) if max_q_len is None else max_q_len
+    pkv.paged_attention_prefill(to_device(q, c.q_dtype), torch.from_numpy(cu).cuda(), mq,
                                 g.k_cache, g.v_cache, g.block_tables, g.context_lens, w.scale, out,
                                 w.max_context_len)
     torch.cuda.synchronize()
@@ -77,6 +78,16 @@ def test_prefill_scale_values(orc, scale):
     print(f"prefill scale {scale}", flush=True)
     w, _, _, got, ref = _run(orc, cfg, (40, 64, 33), scale=scale)
     assert_close_to_oracle(got, ref, "bf16", f"prefill scale {scale}")
+
+
+def test_prefill_empty_chunks_and_loose_bound(orc):
+    """Sequences with no query tokens in the step (empty chunks, no output rows) beside
+    others, and a max_q_len above every chunk (it only sizes the grid)."""
+    cfg = LLAMA8B.replace(num_seqs=4, ctx_kind="fixed", ctx_params=(40, 130, 300, 17))
+    print("prefill empty chunks", flush=True)
+    w, _, cu, got, ref = _run(orc, cfg, (0, 64, 0, 17), max_q_len=200)
+    assert list(cu) == [0, 0, 64, 64, 81]
+    assert_close_to_oracle(got, ref, "bf16", "prefill empty chunks")
 
 
 def test_one_token_chunks_match_decode(orc):
