@@ -8,8 +8,12 @@ seeded, resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout:
   value        effective KV GB/s of the step = algorithmic bytes of a step / step time
-  roofline     the decode call (its dominant kernel) against the 8 TB/s HBM peak,
-               timed with HIP events on its own stream, L2/MALL flushed before each rep
+  roofline     the decode call (its dominant kernel) against the 8 TB/s HBM peak: its
+               average duration over back-to-back calls on 4 copies of the layer's cache
+               taken in turn (each call reads cold data, as consecutive layers do), HIP
+               events on the stream it runs on; single launches after an L2/MALL flush
+               are reported beside it
+  read_ceiling the same tiles read by a streaming-read probe, timed the same way
   cpu_baseline the fp64 oracle timed on this host's cores on a bounded sample
 """
 from __future__ import annotations
@@ -278,10 +282,33 @@ def decode_tiles(w):
     return np.concatenate(out).astype(np.int32)
 
 
-def read_ceiling(w, st, reps):
+LAYERS = 4  # cache copies decoded in turn by the layered leg
+
+
+def layered_ms(run, copies, reps):
+    """Average duration of run(k_cache, v_cache) launched back to back over copies of a
+    layer's cache, taken in turn as a model's layers are decoded: between two uses of a
+    copy the others are read, which evicts it from L2/MALL, so every call reads cold data.
+    HIP events around the whole sequence (on the current stream), divided by the calls."""
+    import torch
+    for k, v in copies:  # warm-up pass: code, tables, workspaces
+        run(k, v)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for k, v in copies:
+            run(k, v)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(copies))
+
+
+def read_ceiling(w, st, reps, copies):
     """Achievable read rate of the decode's K/V access pattern: the streaming-read probe
     (libpkv_probe.so, loads as the decode kernel issues them, no arithmetic) over
-    decode_tiles(w), L2/MALL flushed before each rep, HIP events on the current stream."""
+    decode_tiles(w); single launches after an L2/MALL flush (HIP events on the current
+    stream), and the layered form over the same cache copies as the decode."""
     import ctypes
     import numpy as np
     import torch
@@ -312,8 +339,10 @@ def read_ceiling(w, st, reps):
         e1.record()
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    lay = layered_ms(lambda k, v: f(k.data_ptr(), v.data_ptr(), tiles.data_ptr(), n, tb, sink.data_ptr(), stream),
+                     copies, reps)
     return {"kernel": "pkv_probe_read_tiles", "tiles": n, "tile_bytes": tb, "bytes": 2 * n * tb,
-            "ms_cold_mean": ms, "GBps": 2 * n * tb / (ms * 1e-3) / 1e9}
+            "ms_cold_mean": ms, "ms_layered": lay, "GBps": 2 * n * tb / (lay * 1e-3) / 1e9}
 
 
 def measure(cfg, args, partition=None):
@@ -374,15 +403,30 @@ def measure(cfg, args, partition=None):
         "bytes": nbytes, "schedule": st.schedule,
         "max_context_len": w.max_context_len, "sum_context": int(w.context_lens.sum()),
     }
-    ceil = read_ceiling(w, st, args.reps)
+    # layered leg: LAYERS copies of this layer's cache decoded in turn, back to back
+    copies = [(st.k_cache, st.v_cache)] + [(st.k_cache.clone(), st.v_cache.clone()) for _ in range(LAYERS - 1)]
+    k0, v0 = st.k_cache, st.v_cache
+
+    def run_decode(k, v):
+        st.k_cache, st.v_cache = k, v
+        st.decode()
+    lay_ms = layered_ms(run_decode, copies, max(4, args.reps // LAYERS))
+    st.k_cache, st.v_cache = k0, v0
+    res["decode_ms_layered"] = lay_ms
+    res["decode_GBps_layered"] = nbytes["decode"] / (lay_ms * 1e-3) / 1e9
+    ceil = read_ceiling(w, st, max(4, args.reps // LAYERS), copies)
+    del copies
+    torch.cuda.empty_cache()
     # the same tiles read by the probe alone vs by the decode (which also reads q and the
-    # tables and computes): the decode's fraction of the pattern's achievable rate
-    ceil["decode_frac"] = ceil["ms_cold_mean"] / dec_ms
+    # tables and computes), both layered: the decode's fraction of the pattern's rate
+    ceil["decode_frac"] = ceil["ms_layered"] / lay_ms
     res["read_ceiling"] = ceil
     log(f"[{cfg.name}] step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s), decode cold "
         f"{dec_ms * 1e3:.1f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak), "
-        f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, schedule {res['schedule']}; read ceiling of its "
-        f"tiles {ceil['GBps']:.0f} GB/s ({ceil['ms_cold_mean'] * 1e3:.1f} us), decode at "
+        f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, schedule {res['schedule']}; layered decode "
+        f"{lay_ms * 1e3:.1f} us ({res['decode_GBps_layered']:.0f} GB/s, "
+        f"{100 * res['decode_GBps_layered'] / HBM_PEAK_GBS:.1f}%); read ceiling of its tiles "
+        f"{ceil['GBps']:.0f} GB/s ({ceil['ms_layered'] * 1e3:.1f} us layered), decode at "
         f"{100 * ceil['decode_frac']:.1f}% of it")
     return w, st, res
 
@@ -616,12 +660,17 @@ def main():
                    "seed": c.seed, **({"window": c.window, "sinks": c.sinks} if c.window else {})},
         "pct_hbm_peak": round(100 * res["step_GBps"] / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(res["seq_heads_per_s"], 1),
-        "roofline": {"bound": "hbm", "achieved": round(res["decode_GBps_cold"], 2),
+        # achieved: the decode call's average duration over back-to-back calls on cold
+        # per-layer cache copies (the layered leg); the single-launch figure beside it
+        "roofline": {"bound": "hbm", "achieved": round(res["decode_GBps_layered"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(res["decode_frac_hbm_peak"], 4), "traffic": traffic,
+                     "frac": round(res["decode_GBps_layered"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": kernel_label(res["schedule"]),
                      "bytes_per_launch": res["bytes"]["decode"],
-                     "mean_launch_ms": round(res["decode_ms_cold_mean"], 6)},
+                     "mean_launch_ms": round(res["decode_ms_layered"], 6),
+                     "timing": f"mean over back-to-back calls on {LAYERS} cold per-layer cache copies",
+                     "single_launch_ms": round(res["decode_ms_cold_mean"], 6),
+                     "single_launch_GBps": round(res["decode_GBps_cold"], 2)},
         "cpu_baseline": cpu,
         "read_ceiling": {k: (round(v, 4) if isinstance(v, float) else v)
                          for k, v in res["read_ceiling"].items()},
