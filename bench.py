@@ -37,7 +37,7 @@ DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 CSRC = "paged_kv_cache_27_amd/csrc"
 KERNEL_SOURCES = [f"{CSRC}/{n}" for n in (
     "decode.hip", "decode_sk.hip", "decode_sk_kernel.h", "decode_sk_bf16.hip", "decode_sk_f16.hip",
-    "decode_sk_pre.hip", "mfma_rows.hip",
+    "decode_sk_pre.hip", "decode_sk_pre_fp8.hip", "mfma_rows.hip",
     "decode_sk_f32.hip", "decode_sk_fp8_qbf16.hip", "decode_sk_fp8_qf16.hip", "decode_common.h",
     "pkv_device.h", "pkv_launch.h", "api.cpp")]
 

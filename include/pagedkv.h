@@ -230,9 +230,9 @@ int paged_attention_decode_window(const void* q, pkv_dtype q_dtype, int32_t num_
  *   workspace      : >= paged_attention_shared_prefix_workspace_size() bytes, 256-byte
  *                    aligned, first PKV_WORKSPACE_HEADER_BYTES zero (as for
  *                    paged_attention_decode); never NULL
- * Supported: the 16-bit caches ((bf16, bf16), (f16, f16)); head_dim, block_size and
- * group size as for paged_attention_decode; up to 8191 sequences.  Other dtypes
- * return PKV_ERR_DTYPE.  The grouping only selects the work split: any grouping that
+ * Supported (query, cache): (bf16, bf16), (f16, f16), (bf16 or f16, fp8 e4m3fn with the
+ * descriptor's k_scale / v_scale); head_dim, block_size and group size as for
+ * paged_attention_decode; up to 8191 sequences.  fp32 caches return PKV_ERR_DTYPE.  The grouping only selects the work split: any grouping that
  * meets the preconditions gives the same attention, to within fp32 rounding order.
  * Preconditions beyond those of paged_attention_decode are not checked on the device.
  */
@@ -262,9 +262,10 @@ int paged_attention_decode_shared_prefix(
  *   max_q_len    : host-side upper bound of n_s (sizes the grid), <= max_context_len
  *   context_lens : int32 [num_seqs], counting the chunk (n_s <= context_lens[s])
  *   out          : [rows][num_q_heads][head_dim] of out_dtype (f32/f16/bf16)
- * Other arguments as paged_attention_decode.  Supported: 16-bit caches ((bf16, bf16),
- * (f16, f16)); head_dim 64 or 128; block_size 16 or 32; group size 1..16.  Other cache
- * dtypes return PKV_ERR_DTYPE.  No workspace.  Preconditions (unchecked on the device):
+ * Other arguments as paged_attention_decode.  Supported (query, cache): (bf16, bf16),
+ * (f16, f16), (bf16 or f16, fp8 e4m3fn with the descriptor's k_scale / v_scale); head_dim
+ * 64 or 128; block_size 16 or 32; group size 1..16.  fp32 caches return PKV_ERR_DTYPE.
+ * No workspace.  Preconditions (unchecked on the device):
  * n_s <= max_q_len and n_s <= context_lens[s]; block IDs in range for the tokens read.
  */
 int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,

@@ -210,10 +210,12 @@ def paged_kv_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 def paged_attention_prefill(q: torch.Tensor, cu_q: torch.Tensor, max_q_len: int, k_cache: torch.Tensor,
                             v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                             scale: float, out: torch.Tensor, max_context_len: int, q_dtype=None,
-                            out_dtype=None, stream=None) -> torch.Tensor:
-    """Chunked-prefill attention into `out` ([rows][H_q][D]); see include/pagedkv.h."""
+                            out_dtype=None, kv_dtype=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                            stream=None) -> torch.Tensor:
+    """Chunked-prefill attention into `out` ([rows][H_q][D]); see include/pagedkv.h.
+    kv_dtype / k_scale / v_scale describe an fp8 cache as for paged_attention_decode."""
     lib = load_library()
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
     rows, hq, d = q.shape
     assert cu_q.dtype == torch.int32 and block_tables.dtype == torch.int32
     assert context_lens.dtype == torch.int32
@@ -414,12 +416,14 @@ def paged_attention_decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor,
                                          group_starts: torch.Tensor, prefix_lens: torch.Tensor,
                                          max_group_size: int, max_prefix_len: int,
                                          workspace: torch.Tensor | None = None, q_dtype=None,
-                                         out_dtype=None, stream=None) -> torch.Tensor:
+                                         out_dtype=None, kv_dtype=None, k_scale: float = 1.0,
+                                         v_scale: float = 1.0, stream=None) -> torch.Tensor:
     """Decode attention into `out` for prefix-sharing groups (see include/pagedkv.h).
     group_starts: int32 [num_groups + 1]; prefix_lens: int32 [num_seqs].  `workspace`
-    (zero-headed, as for paged_attention_decode) is allocated by torch when not given."""
+    (zero-headed, as for paged_attention_decode) is allocated by torch when not given.
+    kv_dtype / k_scale / v_scale describe an fp8 cache as for paged_attention_decode."""
     lib = load_library()
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
     n, hq, d = q.shape
     qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
     ng = group_starts.numel() - 1

@@ -118,7 +118,7 @@ struct PrefixPlan {
 int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
                 int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
                 int32_t max_prefix_len, PrefixPlan* out) {
-  if (c->dtype != PKV_BF16 && c->dtype != PKV_F16) return PKV_ERR_DTYPE;
+  if (c->dtype == PKV_F32) return PKV_ERR_DTYPE;  // 16-bit and fp8 caches (queries checked as decode)
   if (num_groups < 1 || max_group_size < 1 || max_prefix_len < 0) return PKV_ERR_SHAPE;
   if (max_prefix_len % c->block_size != 0 || max_prefix_len > max_context_len) return PKV_ERR_SHAPE;
   if (num_seqs > pkv::kStreamKMaxSeqs || num_groups > num_seqs) return PKV_ERR_SHAPE;
@@ -145,7 +145,7 @@ int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
 }
 
 // Arguments common to both uses of the rows kernel; the use-specific ones stay null.
-pkv::RowsArgs rows_args(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+pkv::RowsArgs rows_args(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
                         const void* v_cache, const pkv_cache_desc* c, const int32_t* block_tables,
                         int32_t max_blocks_per_seq, float scale, int32_t tiles, hipStream_t stream) {
   pkv::RowsArgs p;
@@ -156,6 +156,9 @@ pkv::RowsArgs rows_args(const void* q, int32_t num_seqs, int32_t num_q_heads, co
   p.head_dim = c->head_dim;
   p.block_size = c->block_size;
   p.cache_dtype = c->dtype;
+  p.q_dtype = q_dtype;
+  p.k_scale = c->dtype == PKV_FP8_E4M3 ? c->k_scale : 1.0f;
+  p.v_scale = c->dtype == PKV_FP8_E4M3 ? c->v_scale : 1.0f;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.block_tables = block_tables;
@@ -424,7 +427,7 @@ int paged_attention_decode_shared_prefix(
 
   float* pre_part = (float*)((char*)workspace + plan.sk.ws_bytes);
   if (max_prefix_len > 0) {
-    pkv::RowsArgs p = rows_args(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+    pkv::RowsArgs p = rows_args(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
                                 max_blocks_per_seq, scale, plan.tiles, stream);
     p.group_starts = group_starts;
     p.prefix_lens = prefix_lens;
@@ -479,7 +482,7 @@ int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, 
                             float scale, void* out, pkv_dtype out_dtype, hipStream_t stream) {
   int st = check_decode_shape(cache, q_dtype, out_dtype, num_seqs, num_q_heads, max_context_len);
   if (st) return st;
-  if (cache->dtype != PKV_BF16 && cache->dtype != PKV_F16) return PKV_ERR_DTYPE;
+  if (cache->dtype == PKV_F32) return PKV_ERR_DTYPE;  // 16-bit and fp8 caches (queries checked as decode)
   if (max_q_len < 0 || max_q_len > max_context_len || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
@@ -488,7 +491,7 @@ int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, 
   const int32_t G = num_q_heads / cache->num_kv_heads;
   const int64_t tiles = ((int64_t)max_q_len * G + pkv::kPrefillRows - 1) / pkv::kPrefillRows;
   if (tiles * num_seqs * cache->num_kv_heads > 0x7fffffff) return PKV_ERR_SHAPE;
-  pkv::RowsArgs p = rows_args(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+  pkv::RowsArgs p = rows_args(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
                               max_blocks_per_seq, scale, (int32_t)tiles, stream);
   p.cu_q = cu_q;
   p.context_lens = context_lens;

@@ -18,12 +18,14 @@ PKV_SK_FOR_DTYPES(PKV_SK_EXTERN, kFP8, kBF16)
 PKV_SK_FOR_DTYPES(PKV_SK_EXTERN, kFP8, kF16)
 PKV_SK_FOR_DTYPES(PKV_SK_EXTERN_PRE, kBF16, kBF16)
 PKV_SK_FOR_DTYPES(PKV_SK_EXTERN_PRE, kF16, kF16)
+PKV_SK_FOR_DTYPES(PKV_SK_EXTERN_PRE, kFP8, kBF16)
+PKV_SK_FOR_DTYPES(PKV_SK_EXTERN_PRE, kFP8, kF16)
 
 // Resolve (cache dtype, q dtype, head dim, padded group, load policy, suffix pass of
 // the shared-prefix decode) to the kernel and run f.
 template <typename F>
 static hipError_t with_sk(int kv, int q, int d, int gp, bool nt, bool pre, F&& f) {
-  if (pre) {  // 16-bit caches, streaming loads
+  if (pre) {  // 16-bit and fp8 caches, streaming loads
 #define PKV_SK_PRE_GP(KV, Q, D)                                       \
   switch (gp) {                                                       \
     case 1: return f(SkKernels<KV, Q, D, 1, true, true>());           \
@@ -40,6 +42,8 @@ static hipError_t with_sk(int kv, int q, int d, int gp, bool nt, bool pre, F&& f
     if (!nt) return hipErrorInvalidValue;
     if (kv == kBF16 && q == kBF16) { PKV_SK_PRE_D(kBF16, kBF16) }
     if (kv == kF16 && q == kF16) { PKV_SK_PRE_D(kF16, kF16) }
+    if (kv == kFP8 && q == kBF16) { PKV_SK_PRE_D(kFP8, kBF16) }
+    if (kv == kFP8 && q == kF16) { PKV_SK_PRE_D(kFP8, kF16) }
 #undef PKV_SK_PRE_D
 #undef PKV_SK_PRE_GP
     return hipErrorInvalidValue;

@@ -59,6 +59,11 @@ template <int KV> struct PfxOps;
 template <> struct PfxOps<kBF16> {
   using frag8 = bf16x8_t;
   static constexpr uint32_t kOne = 0x3f803f80u;
+  // four e4m3fn codes -> four bf16 (exact), as two words of two
+  __device__ __forceinline__ static uint2 from_fp8(uint32_t w) {
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true)));
+  }
   __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -73,6 +78,10 @@ template <> struct PfxOps<kBF16> {
 template <> struct PfxOps<kF16> {
   using frag8 = f16x8_t;
   static constexpr uint32_t kOne = 0x3c003c00u;
+  __device__ __forceinline__ static uint2 from_fp8(uint32_t w) {  // e4m3fn -> f16 is exact too
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true)));
+  }
   __device__ __forceinline__ static f32x4_t qk(frag8 a, frag8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
@@ -120,22 +129,30 @@ constexpr int kRowsDepth = 1;  // steps (32 tokens each) whose loads are in flig
 // (i < 4), and those 8 probabilities are its k-slots 8(l/16) .. 8(l/16)+7 of the
 // 16x16x32 P.V MFMA (the contraction order is free as long as V uses the same one), so
 // V is staged as [lane group g][dim][tokens 4g..4g+3 of A, 4g..4g+3 of B].
-template <int KV, int D, bool PREFILL>
+// KV: cache dtype (bf16, f16, or fp8 e4m3fn with 16-bit queries); QT: query dtype, the
+// 16-bit type the tiles are staged in (fp8 codes convert to it exactly) and the MFMAs
+// run in.
+template <int KV, int QT, int D, bool PREFILL>
 __global__ void __launch_bounds__(64 * kRowsWaves)
     __attribute__((amdgpu_waves_per_eu(RowSets<PREFILL>::waves_per_simd)))
 rows_kernel(const RowsArgs a) {
-  using O_ = PfxOps<KV>;
+  using O_ = PfxOps<QT>;
   using frag8 = typename O_::frag8;
-  constexpr int ROW = 2 * D;           // bytes of one K/V row
+  constexpr int EB = KV == kFP8 ? 1 : 2;  // cache element bytes
+  constexpr int ROW = EB * D;          // bytes of one cache K/V row
+  constexpr int QROW = 2 * D;          // bytes of one query row
   constexpr int NKC = D / 32;          // 16x16x32 MFMAs per 16 tokens of Q.K (K dims)
   constexpr int NJ = D / 16;           // 16-dim output tiles
   constexpr int NT = 64 * kRowsWaves;   // threads of the workgroup
-  constexpr int KPIECES = 32 * (D / 8); // 16-byte pieces of a step's 32 K rows
-  constexpr int KP = KPIECES / NT;      // K pieces per thread (2 for D = 128, 1 for 64)
-  constexpr int VSTAGE = 4 * (D / 2);   // V stagers: 4 lane groups x D/2 dim pairs
+  constexpr int PE = 16 / EB;           // elements of a 16-byte cache piece
+  constexpr int KPIECES = 32 * (D / PE); // 16-byte pieces of a step's 32 K rows
+  constexpr int KP = (KPIECES + NT - 1) / NT;  // K pieces per thread (the last round may be partial)
+  constexpr bool KFULL = KPIECES % NT == 0;     // every thread has a piece in every round
+  constexpr int DPT = 4 / EB;           // V dims per stager (one 32-bit word of each token row)
+  constexpr int VSTAGE = 4 * (D / DPT); // V stagers: 4 lane groups x D/DPT dim groups
   constexpr int KROW = D + 8;           // K row stride in LDS (elements): conflict-free A reads
   constexpr int STRIDE = 4 + D;         // floats per partial: m, l, pad, pad, acc[D]
-  static_assert(KP >= 1 && KPIECES % NT == 0 && VSTAGE <= NT && VSTAGE % 64 == 0,
+  static_assert(KPIECES % 64 == 0 && VSTAGE <= NT && VSTAGE % 64 == 0 && (16 * (D / PE)) % 64 == 0,
                 "staging by whole waves of the workgroup");
   // K as [32 tokens][KROW]; V as [lane group g][dim][8 tokens: 4g..4g+3 of A, of B], 16-bit.
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][32 * KROW];
@@ -189,7 +206,7 @@ rows_kernel(const RowsArgs a) {
   // c = |scale| log2(e) > 0, so the running max can be taken on raw scores: a negative
   // scale flips the sign of Q instead (exact in 16 bits) and a zero scale zeroes Q (all
   // scores 0: the same uniform weights).
-  const float c_l2 = (a.scale != 0.0f ? __builtin_fabsf(a.scale) : 1.0f) * kLog2e;
+  const float c_l2 = (a.scale != 0.0f ? __builtin_fabsf(a.scale) : 1.0f) * kLog2e * a.k_scale;
   const uint32_t qflip = a.scale < 0.0f ? 0x80008000u : 0u;
   const bool qzero = a.scale == 0.0f;
 
@@ -205,7 +222,7 @@ rows_kernel(const RowsArgs a) {
     rq[rs] = wrow0 + 16 * rs + (lane & 15);
     qvalid[rs] = rq[rs] < nrows;
     const uint8_t* qrow = (const uint8_t*)a.q +
-        ((size_t)(qbase + (qvalid[rs] ? rq[rs] / G : 0)) * a.num_q_heads + g * G + (qvalid[rs] ? rq[rs] % G : 0)) * ROW;
+        ((size_t)(qbase + (qvalid[rs] ? rq[rs] / G : 0)) * a.num_q_heads + g * G + (qvalid[rs] ? rq[rs] % G : 0)) * QROW;
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
       uint4 w = make_uint4(0, 0, 0, 0);
@@ -251,11 +268,13 @@ rows_kernel(const RowsArgs a) {
   auto tile_off = [&](int c, uint32_t blk) {
     return (size_t)blk * blk_bytes + (uint32_t)(((16 * min(c, c1 - 1)) & (BS - 1)) * ROW);
   };
-  // Staging: K piece q = tid + NT k (k < KP) is row q / (D/8) (chunk A for rows < 16, B
-  // after), 16-byte piece q % (D/8); V stager (gg, dp) = (tid / (D/2), tid % (D/2))
-  // loads tokens 4gg .. 4gg+3 of A and of B, dims 2dp, 2dp+1.  Every thread issues all
-  // its loads, the ones it has no part in through an empty resource.
-  const int gg = (tid / (D / 2)) & 3, dp = tid % (D / 2);
+  // Staging: K piece q = tid + NT k (k < KP, q < KPIECES) is row q / (D/PE) (chunk A for
+  // rows < 16, B after), 16-byte piece q % (D/PE); V stager (gg, dp) = (tid / (D/DPT),
+  // tid % (D/DPT)) loads tokens 4gg .. 4gg+3 of A and of B, dims DPT dp .. DPT dp + DPT-1
+  // (one 32-bit word of each row).  Every thread issues all its loads, the ones it has no
+  // part in through an empty resource.  fp8 codes become the query's 16-bit type on the
+  // way into LDS.
+  const int gg = (tid / (D / DPT)) & 3, dp = tid % (D / DPT);
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const bool vstage = tid < VSTAGE;
   struct Stage {
@@ -268,13 +287,16 @@ rows_kernel(const RowsArgs a) {
     const size_t oa = tile_off(cA, bk.a), ob = tile_off(cA + 1, bk.b);
     const __amdgpu_buffer_rsrc_t ka = tile_rsrc(kc + oa, la ? 16 * ROW : 0);
     const __amdgpu_buffer_rsrc_t kb = tile_rsrc(kc + ob, lb ? 16 * ROW : 0);
+    const __amdgpu_buffer_rsrc_t none = tile_rsrc(kc, 0);
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
-      const int q = tid + NT * k, r = q / (D / 8), pc = q % (D / 8);
-      // rows < 16 (pieces q < 2 D) are chunk A; 2 D is a multiple of 64, so a whole
-      // wave's pieces fall in one chunk (a scalar select of the two resources)
-      const bool in_a = 64 * wvu + NT * k < 2 * D;
-      st.k[k] = load_kv16<false>(in_a ? ka : kb, (r & 15) * ROW + 16 * pc);
+      const int q = tid + NT * k, r = q / (D / PE), pc = q % (D / PE);
+      // rows < 16 (pieces q < 16 D/PE, a multiple of 64) are chunk A, so a whole wave's
+      // pieces fall in one chunk (a scalar select of the resources), and so does the
+      // bound q < KPIECES of a partial last round
+      const bool in_a = 64 * wvu + NT * k < 16 * (D / PE);
+      const bool kact = KFULL || 64 * wvu + NT * k < KPIECES;
+      st.k[k] = load_kv16<false>(kact ? (in_a ? ka : kb) : none, (r & 15) * ROW + 16 * pc);
     }
     const __amdgpu_buffer_rsrc_t va = tile_rsrc(vc + oa, la && vstage ? 16 * ROW : 0);
     const __amdgpu_buffer_rsrc_t vb = tile_rsrc(vc + ob, lb && vstage ? 16 * ROW : 0);
@@ -290,8 +312,16 @@ rows_kernel(const RowsArgs a) {
   auto stage = [&](int buf, int cA, const Stage& st) {
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
-      const int q = tid + NT * k, r = q / (D / 8), pc = q % (D / 8);
-      *(uint4*)&lds_k[buf][r * KROW + 8 * pc] = st.k[k];
+      const int q = tid + NT * k, r = q / (D / PE), pc = q % (D / PE);
+      if (!KFULL && 64 * wvu + NT * k >= KPIECES) continue;  // wave-uniform
+      if constexpr (EB == 2) {
+        *(uint4*)&lds_k[buf][r * KROW + 8 * pc] = st.k[k];
+      } else {  // 16 codes -> 16 elements: two 16-byte writes
+        const uint2 x0 = O_::from_fp8(st.k[k].x), x1 = O_::from_fp8(st.k[k].y);
+        const uint2 x2 = O_::from_fp8(st.k[k].z), x3 = O_::from_fp8(st.k[k].w);
+        *(uint4*)&lds_k[buf][r * KROW + 16 * pc] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        *(uint4*)&lds_k[buf][r * KROW + 16 * pc + 8] = make_uint4(x2.x, x2.y, x3.x, x3.y);
+      }
     }
     if (vstage) {
       uint32_t w[8];
@@ -302,18 +332,34 @@ rows_kernel(const RowsArgs a) {
         for (int e = 0; e < 8; ++e)
           if (16 * (cA + e / 4) + 4 * gg + (e & 3) >= ctx) w[e] = 0u;
       }
-      // dim 2dp: the low halves of the 8 tokens' words, dim 2dp+1: the high halves
-      const uint4 lo = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                                  __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
-                                  __builtin_amdgcn_perm(w[5], w[4], 0x05040100u),
-                                  __builtin_amdgcn_perm(w[7], w[6], 0x05040100u));
-      const uint4 hi = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
-                                  __builtin_amdgcn_perm(w[3], w[2], 0x07060302u),
-                                  __builtin_amdgcn_perm(w[5], w[4], 0x07060302u),
-                                  __builtin_amdgcn_perm(w[7], w[6], 0x07060302u));
-      uint16_t* base = &lds_v[buf][(gg * D + 2 * dp) * 8];
-      *(uint4*)base = lo;
-      *(uint4*)(base + 8) = hi;
+      // x[e]: two 16-bit dims of token e per word; dim 2j of the pair j: the low halves of
+      // the 8 tokens' words, dim 2j+1: the high halves
+      auto put_pair = [&](const uint32_t (&x)[8], int dim) {
+        const uint4 lo = make_uint4(__builtin_amdgcn_perm(x[1], x[0], 0x05040100u),
+                                    __builtin_amdgcn_perm(x[3], x[2], 0x05040100u),
+                                    __builtin_amdgcn_perm(x[5], x[4], 0x05040100u),
+                                    __builtin_amdgcn_perm(x[7], x[6], 0x05040100u));
+        const uint4 hi = make_uint4(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u),
+                                    __builtin_amdgcn_perm(x[3], x[2], 0x07060302u),
+                                    __builtin_amdgcn_perm(x[5], x[4], 0x07060302u),
+                                    __builtin_amdgcn_perm(x[7], x[6], 0x07060302u));
+        uint16_t* base = &lds_v[buf][(gg * D + dim) * 8];
+        *(uint4*)base = lo;
+        *(uint4*)(base + 8) = hi;
+      };
+      if constexpr (EB == 2) {
+        put_pair(w, 2 * dp);
+      } else {  // each word holds 4 codes: dims 4dp .. 4dp+3
+        uint32_t x0[8], x1[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint2 c = O_::from_fp8(w[e]);
+          x0[e] = c.x;
+          x1[e] = c.y;
+        }
+        put_pair(x0, 4 * dp);
+        put_pair(x1, 4 * dp + 2);
+      }
     }
   };
   // One step from LDS buffer buf: S^T = K Q^T for chunks A and B, online softmax over
@@ -455,7 +501,7 @@ rows_kernel(const RowsArgs a) {
         const float li = Ol[rs][i];
         const int rr = wrow0 + 16 * rs + 4 * (lane >> 4) + i;
         if (rr >= nrows) continue;
-        const float inv = li != 0.0f ? 1.0f / li : 0.0f;
+        const float inv = li != 0.0f ? a.v_scale / li : 0.0f;  // fp8: value = code * v_scale
         const size_t o = ((size_t)(qbase + rr / G) * a.num_q_heads + g * G + rr % G) * D + (lane & 15);
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) store_out(a.out, o + 16 * jj, a.out_dtype, O[rs][jj][i] * inv);
@@ -488,12 +534,17 @@ template <bool PREFILL>
 static hipError_t launch_rows(const RowsArgs& a, int64_t grid) {
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 block(64 * kRowsWaves);
-#define PKV_ROWS(KV, D) \
-  hipLaunchKernelGGL((rows_kernel<KV, D, PREFILL>), dim3((unsigned)grid), block, 0, a.stream, a)
-  if (a.cache_dtype == kBF16 && a.head_dim == 128) PKV_ROWS(kBF16, 128);
-  else if (a.cache_dtype == kBF16 && a.head_dim == 64) PKV_ROWS(kBF16, 64);
-  else if (a.cache_dtype == kF16 && a.head_dim == 128) PKV_ROWS(kF16, 128);
-  else if (a.cache_dtype == kF16 && a.head_dim == 64) PKV_ROWS(kF16, 64);
+#define PKV_ROWS(KV, QT)                                                                                 \
+  if (a.head_dim == 128)                                                                                 \
+    hipLaunchKernelGGL((rows_kernel<KV, QT, 128, PREFILL>), dim3((unsigned)grid), block, 0, a.stream, a); \
+  else if (a.head_dim == 64)                                                                             \
+    hipLaunchKernelGGL((rows_kernel<KV, QT, 64, PREFILL>), dim3((unsigned)grid), block, 0, a.stream, a);  \
+  else                                                                                                   \
+    return hipErrorInvalidValue;
+  if (a.cache_dtype == kBF16 && a.q_dtype == kBF16) { PKV_ROWS(kBF16, kBF16) }
+  else if (a.cache_dtype == kF16 && a.q_dtype == kF16) { PKV_ROWS(kF16, kF16) }
+  else if (a.cache_dtype == kFP8 && a.q_dtype == kBF16) { PKV_ROWS(kFP8, kBF16) }
+  else if (a.cache_dtype == kFP8 && a.q_dtype == kF16) { PKV_ROWS(kFP8, kF16) }
   else return hipErrorInvalidValue;
 #undef PKV_ROWS
   return hipGetLastError();

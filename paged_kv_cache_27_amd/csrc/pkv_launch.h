@@ -59,7 +59,8 @@ struct DecodeArgs {
 struct RowsArgs {
   const void* q;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
-  int cache_dtype;
+  int cache_dtype, q_dtype;
+  float k_scale, v_scale;  // fp8 caches: value = code * scale (1 otherwise)
   const void* k_cache;
   const void* v_cache;
   const int32_t* block_tables;

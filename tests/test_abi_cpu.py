@@ -168,7 +168,9 @@ def _prefix_call(lib, desc, q_dtype=pkv.BF16, n=4, hq=4, maxb=8, maxctx=100, gro
 
 def test_shared_prefix_argument_errors():
     lib = pkv.load_library()
-    assert _prefix_call(lib, _desc(dtype=pkv.FP8_E4M3)) == -2  # 16-bit caches only
+    # fp8 caches take bf16 / f16 queries and positive scales (checked before any launch)
+    assert _prefix_call(lib, _desc(dtype=pkv.FP8_E4M3), q_dtype=pkv.F32) == -2
+    assert _prefix_call(lib, _desc(dtype=pkv.FP8_E4M3, v_scale=0.0)) == -3
     assert _prefix_call(lib, _desc(dtype=pkv.F32), q_dtype=pkv.F32) == -2
     assert _prefix_call(lib, _desc(), pmax=24) == -3  # not a multiple of the block size
     assert _prefix_call(lib, _desc(), pmax=112) == -3  # longer than the longest context
@@ -182,6 +184,8 @@ def test_shared_prefix_argument_errors():
     assert _prefix_call(lib, _desc(), wsb=need - 1) == -5
     assert _prefix_call(lib, _desc(), n=0) == 0
     assert pkv.paged_attention_shared_prefix_workspace_size(_desc(dtype=pkv.FP8_E4M3), pkv.BF16,
+                                                            4, 4, 100, 1, 4, 32) > pkv.WORKSPACE_HEADER_BYTES
+    assert pkv.paged_attention_shared_prefix_workspace_size(_desc(dtype=pkv.F32), pkv.F32,
                                                             4, 4, 100, 1, 4, 32) == 0
 
 
@@ -193,7 +197,8 @@ def _prefill_call(lib, desc, q_dtype=pkv.BF16, n=2, hq=4, cu=FAKE, maxq=16, maxb
 
 def test_prefill_argument_errors():
     lib = pkv.load_library()
-    assert _prefill_call(lib, _desc(dtype=pkv.FP8_E4M3)) == -2  # 16-bit caches only
+    assert _prefill_call(lib, _desc(dtype=pkv.FP8_E4M3), q_dtype=pkv.F32) == -2  # fp8: 16-bit queries
+    assert _prefill_call(lib, _desc(dtype=pkv.FP8_E4M3, k_scale=0.0)) == -3
     assert _prefill_call(lib, _desc(dtype=pkv.F32), q_dtype=pkv.F32) == -2
     assert _prefill_call(lib, _desc(), q_dtype=pkv.F16) == -2  # q dtype != cache dtype
     assert _prefill_call(lib, _desc(), out_dtype=pkv.FP8_E4M3) == -2

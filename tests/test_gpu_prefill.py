@@ -1,7 +1,8 @@
 """Chunked-prefill attention over the paged cache vs the oracle, through the C ABI (GPU
 only).  Each sequence's chunk is the last n_s tokens of its context (written to the
 cache first, with the same write kernel), and query i attends to tokens 0 .. its own
-position.  Bar: 4e-3 * max(1, |ref|) element by element."""
+position.  Bar: 4e-3 * max(1, |ref|) element by element (2e-2 over fp8 caches, as for
+decode)."""
 import dataclasses
 import os
 
@@ -12,7 +13,7 @@ import torch
 import paged_kv_cache_27_amd as pkv
 from gpu_helpers import GpuStep, assert_close_to_oracle, out_to_f64, to_device, torch_dtype
 from helpers import oracle_step
-from workloads import LLAMA8B, PREFIX, TINY, make_workload, prefill_queries
+from workloads import LLAMA8B, PREFIX, R70B_FP8, TINY, make_workload, prefill_queries
 
 pytestmark = pytest.mark.gpu
 THREADS = min(16, len(os.sched_getaffinity(0)))
@@ -37,13 +38,14 @@ def _run(orc, cfg, chunk_lens, seed=77, scale=None, max_q_len=None):
     mq = int(np.max(chunk_lens)) if max_q_len is None else max_q_len
     pkv.paged_attention_prefill(to_device(q, c.q_dtype), torch.from_numpy(cu).cuda(), mq,
                                 g.k_cache, g.v_cache, g.block_tables, g.context_lens, w.scale, out,
-                                w.max_context_len)
+                                w.max_context_len, kv_dtype=g.kv_dtype, k_scale=w.k_scale,
+                                v_scale=w.v_scale)
     torch.cuda.synchronize()
     got = out_to_f64(out)
     del g
     kc, vc, _, _ = oracle_step(orc, w, pairs=np.zeros((0, 2), np.int32))
     ref = orc.prefill(q, c.q_dtype, cu, kc, vc, c.kv_dtype, w.block_tables, w.context_lens, w.scale,
-                      threads=THREADS)
+                      w.k_scale, w.v_scale, threads=THREADS)
     return w, q, cu, got, ref
 
 
@@ -58,6 +60,9 @@ CASES = {
                       (150, 48), (150, 20)),
     "g16-b32": (PREFIX.replace(name="g16", num_q_heads=32, num_kv_heads=2, ctx_kind="fixed"), (300, 97, 33),
                 (96, 97, 5)),
+    "fp8-bf16q-g8": (R70B_FP8, CTX, (1, 16, 17, 64, 100, 64)),
+    "fp8-f16q-d64-b32": (R70B_FP8.replace(name="fp8-f16", head_dim=64, block_size=32, q_dtype="f16",
+                                          out_dtype="f16"), (33, 90, 7, 200), (33, 45, 7, 130)),
 }
 
 

@@ -1,7 +1,8 @@
 """Shared-prefix (cascade) decode vs the oracle, through the C ABI (GPU only).
 
 The entry point must compute exactly what plain decode computes; the bar is the same
-(4e-3 * max(1, |ref|) against the fp64 oracle, element by element).  The groupings
+(4e-3 * max(1, |ref|) against the fp64 oracle, element by element; 2e-2 over fp8
+caches).  The groupings
 passed to it vary independently of how the cache actually shares blocks, as long as
 the declared sharing is real: the true grouping, finer groups, a shorter declared
 prefix, singleton groups without a prefix, and prefixes that cover whole contexts.
@@ -39,7 +40,7 @@ def _run(g, starts, prefix_lens, out=None, workspace=None, scale=None):
     pkv.paged_attention_decode_shared_prefix(
         g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens, scale, out, w.max_context_len,
         torch.from_numpy(starts).cuda(), torch.from_numpy(prefix_lens).cuda(), gmax, pmax,
-        workspace=workspace)
+        workspace=workspace, kv_dtype=g.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
     torch.cuda.synchronize()
     return out
 
@@ -69,6 +70,9 @@ CASES = {
     "mha-g1": PREFIX.replace(num_seqs=5, num_q_heads=4, num_kv_heads=4, ctx_params=(96, 0, 40)),
     "g3": PREFIX.replace(num_seqs=6, num_q_heads=12, num_kv_heads=4, ctx_params=(64, 0, 40)),
     "many-rows": PREFIX.replace(num_seqs=80, prefix_groups=2, ctx_params=(192, 0, 45)),
+    "fp8-bf16q": PREFIX.replace(num_seqs=11, prefix_groups=3, kv_dtype="fp8", ctx_params=(96, 0, 90)),
+    "fp8-f16q-d64-g8": PREFIX.replace(num_seqs=7, head_dim=64, num_q_heads=8, num_kv_heads=1, q_dtype="f16",
+                                      kv_dtype="fp8", out_dtype="f16", ctx_params=(64, 0, 33)),
 }
 
 
