@@ -91,14 +91,15 @@ typedef struct {
 
 /*
  * slot_mapping[t] = block_tables[seq_ids[t]][positions[t] / B] * B + positions[t] % B
- * for each of num_tokens tokens; a negative position gives slot -1 ("skip").
+ * for each of num_tokens tokens; a negative position or sequence ID, or a position
+ * whose block index is >= max_blocks_per_seq, gives slot -1 ("skip").
  * Source: "Optimizacion de Inferencia LLM", section "PagedAttention: Conceptos de
  * SO...", BlockTable.get_physical_block.
  *   seq_ids, positions : int32 [num_tokens]
  *   block_tables       : int32 [num_seqs][max_blocks_per_seq]
  *   slot_mapping       : int64 [num_tokens] (output)
- * Preconditions (not checked on the device): seq_ids in range and
- * positions[t] / B < max_blocks_per_seq.  num_tokens == 0 launches nothing.
+ * Precondition (not checked on the device): seq_ids[t] < num_seqs.  num_tokens == 0
+ * launches nothing.
  */
 int paged_kv_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -110,12 +111,13 @@ int paged_kv_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int3
  * table)" (a new token fills the last block's free slot or the first slot of a
  * freshly appended block); "Capitulo 2", section "Que guarda realmente el KV
  * cache" (the new k_t, v_t join the cached state).
- *   slot_mapping : int64 [num_tokens]; a negative slot skips that token
+ *   slot_mapping : int64 [num_tokens]; a negative slot, or one >= num_blocks * B,
+ *                  skips that token
  *   k, v         : [num_tokens][num_kv_heads][head_dim] of src_dtype (f32/f16/bf16)
  *   k_cache, v_cache : the cache described by `cache`
  * Conversion: same dtype -> bit copy; fp8 cache -> e4m3fn of fl32(fl32(x) / scale)
  * rounded to nearest-even, saturated to +-448, NaN kept NaN.
- * Preconditions (not checked on the device): slots unique and < num_blocks * B.
+ * Precondition (not checked on the device): slots unique.
  */
 int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* k,
                    const void* v, pkv_dtype src_dtype, void* k_cache, void* v_cache,
@@ -276,8 +278,9 @@ int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, 
 
 /* ---------------------------------------------------------------- block moves ---
  * Whole physical blocks of one layer's K and V caches (block_bytes = num_kv_heads *
- * block_size * head_dim * element bytes each).  IDs are int32 device arrays; a
- * negative ID skips its pair or row.  Asynchronous on `stream`; no allocation.
+ * block_size * head_dim * element bytes each).  IDs are int32 device arrays; an ID
+ * outside [0, num_blocks) skips its pair or row.  Asynchronous on `stream`; no
+ * allocation.
  *
  * Copy-on-write: block src_ids[i] -> block dst_ids[i] in both caches, so a sequence
  * about to write into a block it shares gets a private copy first ("PagedAttention por

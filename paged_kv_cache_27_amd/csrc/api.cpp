@@ -233,6 +233,7 @@ int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* 
   a.num_kv_heads = cache->num_kv_heads;
   a.head_dim = cache->head_dim;
   a.block_size = cache->block_size;
+  a.num_blocks = cache->num_blocks;
   a.k_scale = cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f;
   a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
   hipError_t e = pkv::launch_kv_write(a, stream);
@@ -248,7 +249,7 @@ int paged_kv_copy_blocks(const int32_t* src_ids, const int32_t* dst_ids, int32_t
   if (!src_ids || !dst_ids || !k_cache || !v_cache) return PKV_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
   hipError_t e = pkv::launch_move_blocks(k_cache, v_cache, src_ids, k_cache, v_cache, dst_ids, num_pairs,
-                                         block_bytes(cache), stream);
+                                         block_bytes(cache), cache->num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -262,7 +263,7 @@ int paged_kv_swap_out(const int32_t* ids, int32_t num, const void* k_cache, cons
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
     return PKV_ERR_SHAPE;
   hipError_t e = pkv::launch_move_blocks(k_cache, v_cache, ids, k_buf, v_buf, nullptr, num,
-                                         block_bytes(cache), stream);
+                                         block_bytes(cache), cache->num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -276,7 +277,7 @@ int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const v
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
     return PKV_ERR_SHAPE;
   hipError_t e = pkv::launch_move_blocks(k_buf, v_buf, nullptr, k_cache, v_cache, ids, num,
-                                         block_bytes(cache), stream);
+                                         block_bytes(cache), cache->num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -13,7 +13,7 @@
 //     RAM and come back when it resumes).  The buffer may be device memory or pinned
 //     host memory (then the kernel's stores and loads cross PCIe).
 // One workgroup moves one block of one cache with 16-byte accesses, four in flight per
-// thread.  A negative ID skips its pair or row.
+// thread.  An ID outside [0, num_blocks) skips its pair or row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,11 +26,12 @@ constexpr int kMoveThreads = 256;
 // src / dst: base addresses; a null ID array means "row i of a contiguous buffer".
 __global__ void __launch_bounds__(kMoveThreads)
 move_blocks_kernel(const uint8_t* k_src, const uint8_t* v_src, const int32_t* src_ids, uint8_t* k_dst,
-                   uint8_t* v_dst, const int32_t* dst_ids, int64_t block_bytes) {
+                   uint8_t* v_dst, const int32_t* dst_ids, int64_t block_bytes, int64_t num_blocks) {
   const int64_t i = blockIdx.x;
   const int64_t s = src_ids ? (int64_t)src_ids[i] : i;
   const int64_t d = dst_ids ? (int64_t)dst_ids[i] : i;
-  if (s < 0 || d < 0) return;
+  // IDs address the cache side; buffer rows i < num are always in range
+  if (s < 0 || d < 0 || (src_ids && s >= num_blocks) || (dst_ids && d >= num_blocks)) return;
   const uint4* from = (const uint4*)((blockIdx.y == 0 ? k_src : v_src) + s * block_bytes);
   uint4* to = (uint4*)((blockIdx.y == 0 ? k_dst : v_dst) + d * block_bytes);
   const int64_t n = block_bytes / 16;
@@ -48,10 +49,10 @@ move_blocks_kernel(const uint8_t* k_src, const uint8_t* v_src, const int32_t* sr
 
 hipError_t launch_move_blocks(const void* k_src, const void* v_src, const int32_t* src_ids, void* k_dst,
                               void* v_dst, const int32_t* dst_ids, int32_t num, int64_t block_bytes,
-                              hipStream_t stream) {
+                              int64_t num_blocks, hipStream_t stream) {
   hipLaunchKernelGGL(move_blocks_kernel, dim3((unsigned)num, 2), dim3(kMoveThreads), 0, stream,
                      (const uint8_t*)k_src, (const uint8_t*)v_src, src_ids, (uint8_t*)k_dst,
-                     (uint8_t*)v_dst, dst_ids, block_bytes);
+                     (uint8_t*)v_dst, dst_ids, block_bytes, num_blocks);
   return hipGetLastError();
 }
 

@@ -20,12 +20,13 @@ slot_mapping_kernel(const int32_t* __restrict__ seq_ids, const int32_t* __restri
                     int64_t* __restrict__ slot_mapping) {
   const int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= num_tokens) return;
-  const int32_t pos = positions[t];
-  if (pos < 0) {
+  const int32_t pos = positions[t], seq = seq_ids[t];
+  // no slot: a negative position or sequence ID, or a position past the table's row
+  if (pos < 0 || seq < 0 || pos / block_size >= max_blocks_per_seq) {
     slot_mapping[t] = -1;
     return;
   }
-  const int64_t entry = (int64_t)seq_ids[t] * max_blocks_per_seq + pos / block_size;
+  const int64_t entry = (int64_t)seq * max_blocks_per_seq + pos / block_size;
   slot_mapping[t] = (int64_t)block_tables[entry] * block_size + pos % block_size;
 }
 
@@ -35,8 +36,8 @@ __global__ void __launch_bounds__(256)
 kv_write_kernel(const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
                 const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                 uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float k_scale,
-                float v_scale) {
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_slots,
+                float k_scale, float v_scale) {
   constexpr int SB = DtInfo<SRC>::bytes;
   constexpr int DB = DtInfo<DST>::bytes;
   const int32_t per_row = head_dim / 8;
@@ -48,7 +49,7 @@ kv_write_kernel(const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
     const int64_t t = row / num_kv_heads;
     const int32_t h = (int32_t)(row - t * num_kv_heads);
     const int64_t slot = slot_mapping[t];
-    if (slot < 0) continue;
+    if (slot < 0 || slot >= num_slots) continue;  // no slot, or none of this cache's
     const int64_t blk = slot / block_size;
     const int32_t off = (int32_t)(slot - blk * block_size);
     const int64_t src = (row * head_dim + d0) * SB;
@@ -104,7 +105,8 @@ static hipError_t launch_write_t(const WriteArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((kv_write_kernel<SRC, DST>), dim3((unsigned)blocks), dim3(threads), 0,
                      stream, a.slot_mapping, a.num_tokens, (const uint8_t*)a.k,
                      (const uint8_t*)a.v, (uint8_t*)a.k_cache, (uint8_t*)a.v_cache,
-                     a.num_kv_heads, a.head_dim, a.block_size, a.k_scale, a.v_scale);
+                     a.num_kv_heads, a.head_dim, a.block_size, a.num_blocks * a.block_size, a.k_scale,
+                     a.v_scale);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ struct WriteArgs {
   void* v_cache;
   int cache_dtype;
   int32_t num_kv_heads, head_dim, block_size;
+  int64_t num_blocks;
   float k_scale, v_scale;
 };
 
@@ -87,9 +88,11 @@ hipError_t launch_prefill(const RowsArgs& a);
 // Whole-block moves (copy-on-write, swap): pair i moves block src_ids[i] (row i when
 // src_ids is null) of each of the K and V sources to block dst_ids[i] (row i when
 // dst_ids is null) of the destinations; a negative ID skips the pair.
+// An ID array's entries address blocks [0, num_blocks) of that side's cache; the others
+// are skipped.  A null ID array means row i of a contiguous buffer.
 hipError_t launch_move_blocks(const void* k_src, const void* v_src, const int32_t* src_ids, void* k_dst,
                               void* v_dst, const int32_t* dst_ids, int32_t num, int64_t block_bytes,
-                              hipStream_t stream);
+                              int64_t num_blocks, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int32_t n,
                                const int32_t* block_tables, int32_t max_blocks,

@@ -66,11 +66,13 @@ def test_copy_blocks_bit_exact(orc, cfg):
     n = min(len(live), len(free), 9)
     src = rng.choice(live, size=n, replace=True).astype(np.int32)
     dst = rng.choice(free, size=n, replace=False).astype(np.int32)
-    src[1] = -1  # a skipped pair
+    src[1] = -1  # skipped pairs: a negative ID, IDs at or past num_blocks
+    src[2] = w.num_blocks
+    dst[3] = w.num_blocks + 7
     print(f"copy case {cfg.kv_dtype}: {n} pairs", flush=True)
     pkv.paged_kv_copy_blocks(_ids(src), _ids(dst), g.k_cache, g.v_cache, g.kv_dtype)
     torch.cuda.synchronize()
-    orc.copy_blocks(src, dst, kc, vc)
+    orc.copy_blocks(np.where(src < w.num_blocks, src, -1), np.where(dst < w.num_blocks, dst, -1), kc, vc)
     _assert_caches_equal(g, kc, vc, "copy_blocks")
 
 
@@ -78,12 +80,12 @@ def test_swap_round_trip_through_pinned_host_memory(orc):
     w, g, kc, vc = _prepared(orc, LLAMA8B.replace(num_seqs=2, ctx_params=(64, 200), pool_factor=3.0))
     live = _live_blocks(w)
     free = [b for b in range(w.num_blocks) if b not in set(live)]
-    ids = np.array(live[:5] + [-1], np.int32)
+    ids = np.array(live[:5] + [-1, w.num_blocks], np.int32)  # the last two rows skipped
     shape = (ids.size,) + tuple(g.k_cache.shape[1:])
     kb = torch.zeros(shape, dtype=g.k_cache.dtype, device="cuda")
     vb = torch.zeros_like(kb)
     pkv.paged_kv_swap_out(_ids(ids), g.k_cache, g.v_cache, kb, vb, g.kv_dtype)
-    k_ref, v_ref = orc.swap_out(ids, kc, vc)
+    k_ref, v_ref = orc.swap_out(np.where(ids < w.num_blocks, ids, -1), kc, vc)
     torch.cuda.synchronize()
     assert np.array_equal(cache_bytes(kb)[:5], k_ref.view(np.uint8)[:5])
     assert np.array_equal(cache_bytes(vb)[:5], v_ref.view(np.uint8)[:5])
@@ -94,10 +96,10 @@ def test_swap_round_trip_through_pinned_host_memory(orc):
     vh.copy_(vb, non_blocking=True)
     torch.cuda.synchronize()
     kb2, vb2 = kh.cuda(), vh.cuda()
-    back = np.array(free[:5] + [-1], np.int32)
+    back = np.array(free[:5] + [w.num_blocks + 3, -1], np.int32)
     pkv.paged_kv_swap_in(_ids(back), kb2, vb2, g.k_cache, g.v_cache, g.kv_dtype)
     torch.cuda.synchronize()
-    orc.swap_in(back, k_ref, v_ref, kc, vc)
+    orc.swap_in(np.where(back < w.num_blocks, back, -1), k_ref, v_ref, kc, vc)
     _assert_caches_equal(g, kc, vc, "swap_in")
 
 

@@ -92,15 +92,39 @@ def test_write_fp8_f32_inputs(orc):
     assert np.array_equal(vc.cpu().numpy(), vco)
 
 
-def test_negative_slots_skip(orc):
+@pytest.mark.parametrize("kind", ["negative", "past-the-cache"])
+def test_slots_without_a_cache_row_skip(orc, kind):
+    """Negative slots, and slots at or past num_blocks * B, write nothing."""
     w = make_workload(SMALL["llama8b"])
     g = GpuStep(w)
     c = w.cfg
     before = cache_bytes(g.k_cache).copy()
-    slots = torch.full((c.num_seqs,), -1, dtype=torch.int64, device="cuda")
+    before_v = cache_bytes(g.v_cache).copy()
+    end = w.num_blocks * c.block_size
+    vals = [-1, -2, -(1 << 40)] if kind == "negative" else [end, end + 1, end + c.block_size, 1 << 40]
+    slots = torch.tensor([vals[i % len(vals)] for i in range(c.num_seqs)], dtype=torch.int64, device="cuda")
     pkv.paged_kv_write(slots, g.new_k, g.new_v, g.k_cache, g.v_cache)
     torch.cuda.synchronize()
     assert np.array_equal(cache_bytes(g.k_cache), before)
+    assert np.array_equal(cache_bytes(g.v_cache), before_v)
+
+
+def test_slot_mapping_without_a_table_entry(orc):
+    """A negative position or sequence ID, or a position whose block index is past the
+    table's row, maps to -1; the other tokens map as the oracle does."""
+    w = make_workload(SMALL["llama8b"])
+    c = w.cfg
+    nb = w.block_tables.shape[1]
+    seq = np.array([0, 1, 2, -1, 1, 0, 2, 1], np.int32)
+    pos = np.array([0, 17, 5, 3, -4, nb * c.block_size, nb * c.block_size - 1, 1 << 30], np.int32)
+    bad = (seq < 0) | (pos < 0) | (pos // c.block_size >= nb)
+    got = pkv.paged_kv_slot_mapping(torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                                    torch.from_numpy(w.block_tables).cuda(), c.block_size)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.all(got[bad] == -1)
+    ref = orc.slot_mapping(seq[~bad], pos[~bad], w.block_tables, c.block_size)
+    assert np.array_equal(got[~bad], ref)
 
 
 # --------------------------------------------------------------- decode --------
