@@ -2,8 +2,9 @@
 """Benchmark of one paged-KV decode step on one MI355X.
 
 A step is the whole hot path for one decode layer: slot resolution for the new
-tokens, the scatter-write of their K/V into the paged cache, and decode attention
-(plus the log-sum-exp merge when the context is split).  Inputs are synthetic and
+tokens and the scatter-write of their K/V into the paged cache (one call,
+paged_kv_write_positions), then decode attention (plus the log-sum-exp merge when
+the context is split).  Inputs are synthetic and
 seeded, resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout:
@@ -89,8 +90,8 @@ def window_tokens(ctx, window, sinks):
 def algorithmic_bytes(w):
     """Bytes the method must move: decode reads each sequence's whole context once per KV
     head plus q, out, its block-table entries and context length; the write reads the new
-    K/V and the slots and writes the cache rows; slot resolution reads ids/positions/table
-    entries and writes slots."""
+    K/V and writes the cache rows; slot resolution, inside the write, reads each token's
+    sequence ID, position and table entry."""
     c = w.cfg
     n, hq, hkv, d, B = c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size
     ctx = w.context_lens.astype("int64")
@@ -103,15 +104,16 @@ def algorithmic_bytes(w):
         table = int(((ctx + B - 1) // B).sum()) * 4 + 4 * n
     qo = n * hq * d * (DT_BYTES[c.q_dtype] + DT_BYTES[c.out_dtype])
     decode = kv + table + qo
-    write = n * hkv * d * 2 * (DT_BYTES[c.src_dtype] + DT_BYTES[c.kv_dtype]) + 8 * n
-    slots = n * (4 + 4 + 4 + 8)
+    write = n * hkv * d * 2 * (DT_BYTES[c.src_dtype] + DT_BYTES[c.kv_dtype])
+    slots = n * (4 + 4 + 4)
     unique_kv = w.kv_bytes_unique()
     return {"decode": decode, "kv": kv, "kv_unique": unique_kv, "write": write, "slots": slots,
             "step": decode + write + slots}
 
 
 class Step:
-    """Device-resident inputs of one decode step and the three ABI calls that run it."""
+    """Device-resident inputs of one decode step and the two ABI calls that run it (the
+    write with its slot resolution, then the decode)."""
 
     def __init__(self, w, partition=None, shared_prefix=True):
         import numpy as np
@@ -220,9 +222,13 @@ class Step:
                                         kv_dtype=self.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale,
                                         shared_blocks=self.shared)
 
+    def write_positions(self):
+        w = self.w
+        self.pkv.paged_kv_write_positions(self.new_seq, self.new_pos, self.block_tables, self.new_k, self.new_v,
+                                          self.k_cache, self.v_cache, self.kv_dtype, w.k_scale, w.v_scale)
+
     def step(self):
-        self.slot_map()
-        self.write()
+        self.write_positions()
         self.decode()
 
 
@@ -372,21 +378,18 @@ def measure(cfg, args, partition=None):
     # library launches on (torch's current stream, which the binding passes down).
     flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.reps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.reps)]
     for r in range(args.reps):
         sink.copy_(flush.sum())
         e = ev[r]
         e[0].record()
-        st.slot_map()
+        st.write_positions()
         e[1].record()
-        st.write()
-        e[2].record()
         st.decode()
-        e[3].record()
+        e[2].record()
     torch.cuda.synchronize()
-    t_slot = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    t_write = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    t_dec = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_dec = np.array([e[1].elapsed_time(e[2]) for e in ev])
     del flush
     dec_ms = float(np.mean(t_dec))
     achieved = nbytes["decode"] / (dec_ms * 1e-3) / 1e9
@@ -397,7 +400,7 @@ def measure(cfg, args, partition=None):
         "decode_ms_cold_mean": dec_ms, "decode_ms_cold_median": float(np.median(t_dec)),
         "decode_ms_cold_p10": float(np.percentile(t_dec, 10)),
         "decode_ms_cold_p90": float(np.percentile(t_dec, 90)),
-        "write_ms_cold_mean": float(np.mean(t_write)), "slotmap_ms_cold_mean": float(np.mean(t_slot)),
+        "write_ms_cold_mean": float(np.mean(t_write)),
         "decode_GBps_cold": achieved, "decode_frac_hbm_peak": achieved / HBM_PEAK_GBS,
         "decode_unique_GBps_cold": (nbytes["decode"] - nbytes["kv"] + nbytes["kv_unique"]) / (dec_ms * 1e-3) / 1e9,
         "bytes": nbytes, "schedule": st.schedule,

@@ -124,6 +124,29 @@ int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* 
                    const pkv_cache_desc* cache, hipStream_t stream);
 
 /*
+ * Slot resolution and the write in one launch: token t's slot is resolved as by
+ * paged_kv_slot_mapping (from seq_ids[t], positions[t] and block_tables) inside the
+ * write kernel, and its K and V are stored as by paged_kv_write.  Same sources: the
+ * block-table lookup of "Optimizacion de Inferencia LLM", section "PagedAttention:
+ * Conceptos de SO..." (get_physical_block) and the append of "PagedAttention por
+ * dentro...", section "La tabla de paginas (block table)".
+ *   seq_ids, positions : int32 [num_tokens]
+ *   block_tables       : int32 [num_seqs][max_blocks_per_seq]
+ *   k, v, k_cache, v_cache, cache, src_dtype : as for paged_kv_write
+ *   slot_mapping       : int64 [num_tokens] output of the resolved slots (-1 where
+ *                        none), or NULL when the caller needs no slots
+ * A token with a negative position or sequence ID, a position past the table's row,
+ * or a slot outside the cache writes nothing.  Errors as paged_kv_write, plus
+ * PKV_ERR_SHAPE for max_blocks_per_seq <= 0.  Preconditions (not checked on the
+ * device): seq_ids[t] < num_seqs; resolved slots unique.  num_tokens == 0 launches
+ * nothing.  Asynchronous on `stream`; no allocation.
+ */
+int paged_kv_write_positions(const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq, const void* k,
+                             const void* v, pkv_dtype src_dtype, void* k_cache, void* v_cache,
+                             const pkv_cache_desc* cache, int64_t* slot_mapping, hipStream_t stream);
+
+/*
  * How paged_attention_decode schedules a call with these arguments.  Returns the
  * schedule (0 = one pass per (sequence, KV head), 1 = fixed partitions merged by a
  * second log-sum-exp kernel, 2 = balanced: one workgroup per CU, equal shares of

@@ -23,7 +23,7 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHA
           -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH",
           -7: "PKV_ERR_POOL_EXHAUSTED", -8: "PKV_ERR_BLOCK_STATE"}
 
-EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_attention_schedule",
+EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_kv_write_positions", "paged_attention_schedule",
             "paged_attention_workspace_size", "paged_attention_decode", "paged_attention_decode_window",
             "paged_attention_shared_prefix_workspace_size", "paged_attention_decode_shared_prefix",
             "paged_attention_prefill", "paged_kv_copy_blocks", "paged_kv_swap_out", "paged_kv_swap_in",
@@ -68,6 +68,9 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_kv_write.argtypes = [vp, i32, vp, vp, ctypes.c_int, vp, vp,
                                    ctypes.POINTER(CacheDesc), vp]
     lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_kv_write_positions.argtypes = [vp, vp, i32, vp, i32, vp, vp, ctypes.c_int, vp, vp,
+                                             ctypes.POINTER(CacheDesc), vp, vp]
+    lib.paged_kv_write_positions.restype = ctypes.c_int
     lib.paged_attention_workspace_size.argtypes = [ctypes.POINTER(CacheDesc), ctypes.c_int, i32,
                                                    i32, i32, i32]
     lib.paged_attention_workspace_size.restype = ctypes.c_size_t
@@ -205,6 +208,28 @@ def paged_kv_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check("paged_kv_write",
            lib.paged_kv_write(_ptr(slot_mapping), slot_mapping.numel(), _ptr(k), _ptr(v), src,
                               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def paged_kv_write_positions(seq_ids: torch.Tensor, positions: torch.Tensor, block_tables: torch.Tensor,
+                             k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             kv_dtype=None, k_scale: float = 1.0, v_scale: float = 1.0, src_dtype=None,
+                             slot_mapping: torch.Tensor | None = None, stream=None) -> torch.Tensor | None:
+    """Slot resolution and the write in one launch (see include/pagedkv.h).  The resolved
+    slots go to `slot_mapping` (int64 [num_tokens]) when one is given, which is returned."""
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
+    assert seq_ids.dtype == torch.int32 and positions.dtype == torch.int32
+    assert block_tables.dtype == torch.int32 and seq_ids.numel() == positions.numel()
+    if slot_mapping is not None:
+        assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == seq_ids.numel()
+    src = dtype_code(src_dtype if src_dtype is not None else k.dtype)
+    _check("paged_kv_write_positions",
+           lib.paged_kv_write_positions(_ptr(seq_ids), _ptr(positions), seq_ids.numel(), _ptr(block_tables),
+                                        block_tables.shape[1], _ptr(k), _ptr(v), src, _ptr(k_cache),
+                                        _ptr(v_cache), ctypes.byref(desc),
+                                        _ptr(slot_mapping) if slot_mapping is not None else None,
+                                        _stream(stream)))
+    return slot_mapping
 
 
 def paged_attention_prefill(q: torch.Tensor, cu_q: torch.Tensor, max_q_len: int, k_cache: torch.Tensor,

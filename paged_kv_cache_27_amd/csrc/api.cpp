@@ -144,6 +144,47 @@ int plan_prefix(const pkv_cache_desc* c, int q_dtype, int32_t num_seqs, int32_t 
   return PKV_OK;
 }
 
+// Checks shared by the two write entry points (num_tokens == 0 returns PKV_OK before
+// the pointers are looked at).
+int check_write(int32_t num_tokens, const void* k, const void* v, int src_dtype, const void* k_cache,
+                const void* v_cache, const pkv_cache_desc* cache) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (!known_dtype(src_dtype) || src_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (cache->dtype != src_dtype && cache->dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache) return PKV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+// Write arguments without a slot source (the caller sets one).
+pkv::WriteArgs write_args(int32_t num_tokens, const void* k, const void* v, int src_dtype, void* k_cache,
+                          void* v_cache, const pkv_cache_desc* cache) {
+  pkv::WriteArgs a;
+  a.slot_mapping = nullptr;
+  a.seq_ids = nullptr;
+  a.positions = nullptr;
+  a.block_tables = nullptr;
+  a.max_blocks_per_seq = 0;
+  a.slot_out = nullptr;
+  a.num_tokens = num_tokens;
+  a.k = k;
+  a.v = v;
+  a.src_dtype = src_dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_dtype = cache->dtype;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.num_blocks = cache->num_blocks;
+  a.k_scale = cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f;
+  a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
+  return a;
+}
+
 // Arguments common to both uses of the rows kernel; the use-specific ones stay null.
 pkv::RowsArgs rows_args(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
                         const void* v_cache, const pkv_cache_desc* c, const int32_t* block_tables,
@@ -181,7 +222,7 @@ pkv::RowsArgs rows_args(const void* q, int q_dtype, int32_t num_seqs, int32_t nu
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 6; }
+int32_t pkv_abi_version(void) { return 7; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -212,30 +253,30 @@ int paged_kv_slot_mapping(const int32_t* seq_ids, const int32_t* positions, int3
 int paged_kv_write(const int64_t* slot_mapping, int32_t num_tokens, const void* k,
                    const void* v, pkv_dtype src_dtype, void* k_cache, void* v_cache,
                    const pkv_cache_desc* cache, hipStream_t stream) {
-  int st = check_cache(cache);
-  if (st) return st;
-  if (num_tokens < 0) return PKV_ERR_SHAPE;
-  if (!known_dtype(src_dtype) || src_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (cache->dtype != src_dtype && cache->dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-  if (num_tokens == 0) return PKV_OK;
-  if (!slot_mapping || !k || !v || !k_cache || !v_cache) return PKV_ERR_NULL;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
-    return PKV_ERR_SHAPE;
-  pkv::WriteArgs a;
+  int st = check_write(num_tokens, k, v, src_dtype, k_cache, v_cache, cache);
+  if (st || num_tokens == 0) return st;
+  if (!slot_mapping) return PKV_ERR_NULL;
+  pkv::WriteArgs a = write_args(num_tokens, k, v, src_dtype, k_cache, v_cache, cache);
   a.slot_mapping = slot_mapping;
-  a.num_tokens = num_tokens;
-  a.k = k;
-  a.v = v;
-  a.src_dtype = src_dtype;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.cache_dtype = cache->dtype;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.head_dim = cache->head_dim;
-  a.block_size = cache->block_size;
-  a.num_blocks = cache->num_blocks;
-  a.k_scale = cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f;
-  a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
+  hipError_t e = pkv::launch_kv_write(a, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_kv_write_positions(const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq, const void* k,
+                             const void* v, pkv_dtype src_dtype, void* k_cache, void* v_cache,
+                             const pkv_cache_desc* cache, int64_t* slot_mapping, hipStream_t stream) {
+  int st = check_write(num_tokens, k, v, src_dtype, k_cache, v_cache, cache);
+  if (st) return st;
+  if (max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!seq_ids || !positions || !block_tables) return PKV_ERR_NULL;
+  pkv::WriteArgs a = write_args(num_tokens, k, v, src_dtype, k_cache, v_cache, cache);
+  a.seq_ids = seq_ids;
+  a.positions = positions;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.slot_out = slot_mapping;
   hipError_t e = pkv::launch_kv_write(a, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }

@@ -13,6 +13,18 @@
 
 namespace pkv {
 
+// Slot of token t: block_tables[seq][pos / B] * B + pos % B, or -1 for a negative
+// position or sequence ID or a position past the table's row.
+__device__ __forceinline__ int64_t resolve_slot(const int32_t* __restrict__ seq_ids,
+                                                const int32_t* __restrict__ positions, int64_t t,
+                                                const int32_t* __restrict__ block_tables,
+                                                int32_t max_blocks_per_seq, int32_t block_size) {
+  const int32_t pos = positions[t], seq = seq_ids[t];
+  if (pos < 0 || seq < 0 || pos / block_size >= max_blocks_per_seq) return -1;
+  const int64_t entry = (int64_t)seq * max_blocks_per_seq + pos / block_size;
+  return (int64_t)block_tables[entry] * block_size + pos % block_size;
+}
+
 __global__ void __launch_bounds__(256)
 slot_mapping_kernel(const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions,
                     int32_t num_tokens, const int32_t* __restrict__ block_tables,
@@ -20,20 +32,25 @@ slot_mapping_kernel(const int32_t* __restrict__ seq_ids, const int32_t* __restri
                     int64_t* __restrict__ slot_mapping) {
   const int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= num_tokens) return;
-  const int32_t pos = positions[t], seq = seq_ids[t];
-  // no slot: a negative position or sequence ID, or a position past the table's row
-  if (pos < 0 || seq < 0 || pos / block_size >= max_blocks_per_seq) {
-    slot_mapping[t] = -1;
-    return;
-  }
-  const int64_t entry = (int64_t)seq * max_blocks_per_seq + pos / block_size;
-  slot_mapping[t] = (int64_t)block_tables[entry] * block_size + pos % block_size;
+  slot_mapping[t] = resolve_slot(seq_ids, positions, t, block_tables, max_blocks_per_seq, block_size);
 }
 
+// Where each token goes: the given slots, or (RESOLVE) slots resolved here from
+// sequence IDs, positions and block tables -- the slot resolution and the write in one
+// launch -- and stored to slot_out when it is not null.
+struct SlotSrc {
+  const int64_t* slot_mapping;
+  const int32_t* seq_ids;
+  const int32_t* positions;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  int64_t* slot_out;
+};
+
 // One work item = 8 consecutive elements of one (token, KV head) row, for K and V.
-template <int SRC, int DST>
+template <int SRC, int DST, bool RESOLVE>
 __global__ void __launch_bounds__(256)
-kv_write_kernel(const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
+kv_write_kernel(const SlotSrc ss, int32_t num_tokens,
                 const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                 uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_slots,
@@ -48,7 +65,13 @@ kv_write_kernel(const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
     const int32_t d0 = (int32_t)(it - row * per_row) * 8;
     const int64_t t = row / num_kv_heads;
     const int32_t h = (int32_t)(row - t * num_kv_heads);
-    const int64_t slot = slot_mapping[t];
+    int64_t slot;
+    if constexpr (RESOLVE) {
+      slot = resolve_slot(ss.seq_ids, ss.positions, t, ss.block_tables, ss.max_blocks_per_seq, block_size);
+      if (ss.slot_out && h == 0 && d0 == 0) ss.slot_out[t] = slot;
+    } else {
+      slot = ss.slot_mapping[t];
+    }
     if (slot < 0 || slot >= num_slots) continue;  // no slot, or none of this cache's
     const int64_t blk = slot / block_size;
     const int32_t off = (int32_t)(slot - blk * block_size);
@@ -102,11 +125,17 @@ static hipError_t launch_write_t(const WriteArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / 8);
   int64_t blocks = (items + threads - 1) / threads;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((kv_write_kernel<SRC, DST>), dim3((unsigned)blocks), dim3(threads), 0,
-                     stream, a.slot_mapping, a.num_tokens, (const uint8_t*)a.k,
-                     (const uint8_t*)a.v, (uint8_t*)a.k_cache, (uint8_t*)a.v_cache,
-                     a.num_kv_heads, a.head_dim, a.block_size, a.num_blocks * a.block_size, a.k_scale,
-                     a.v_scale);
+  const SlotSrc ss{a.slot_mapping, a.seq_ids, a.positions, a.block_tables, a.max_blocks_per_seq, a.slot_out};
+  if (a.seq_ids)
+    hipLaunchKernelGGL((kv_write_kernel<SRC, DST, true>), dim3((unsigned)blocks), dim3(threads), 0,
+                       stream, ss, a.num_tokens, (const uint8_t*)a.k, (const uint8_t*)a.v,
+                       (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.num_kv_heads, a.head_dim,
+                       a.block_size, a.num_blocks * a.block_size, a.k_scale, a.v_scale);
+  else
+    hipLaunchKernelGGL((kv_write_kernel<SRC, DST, false>), dim3((unsigned)blocks), dim3(threads), 0,
+                       stream, ss, a.num_tokens, (const uint8_t*)a.k, (const uint8_t*)a.v,
+                       (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.num_kv_heads, a.head_dim,
+                       a.block_size, a.num_blocks * a.block_size, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 

@@ -8,7 +8,12 @@
 namespace pkv {
 
 struct WriteArgs {
-  const int64_t* slot_mapping;
+  const int64_t* slot_mapping;  // given slots; or, when seq_ids is set, slots resolved in the
+  const int32_t* seq_ids;       // write kernel from seq_ids / positions / block_tables (and
+  const int32_t* positions;     // stored to slot_out unless it is null)
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  int64_t* slot_out;
   int32_t num_tokens;
   const void* k;
   const void* v;

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pkv.pkv_abi_version() == 6
+    assert pkv.pkv_abi_version() == 7
 
 
 def test_workspace_header_constant_matches_header():
@@ -129,6 +129,26 @@ def test_write_argument_errors():
     assert f(FAKE, 0, None, None, pkv.BF16, None, None, ctypes.byref(_desc()), None) == 0
     misaligned = ctypes.c_void_p(0x100004)
     assert f(FAKE, 4, misaligned, FAKE, pkv.BF16, FAKE, FAKE, ctypes.byref(_desc()), None) == -3
+
+
+def test_write_positions_argument_errors():
+    lib = pkv.load_library()
+    f = lib.paged_kv_write_positions
+    d = ctypes.byref(_desc())
+    assert f(FAKE, FAKE, 4, FAKE, 4, FAKE, FAKE, pkv.FP8_E4M3, FAKE, FAKE, d, None, None) == -2
+    assert f(FAKE, FAKE, 4, FAKE, 4, FAKE, FAKE, pkv.F16, FAKE, FAKE, d, None, None) == -2
+    assert f(FAKE, FAKE, 4, FAKE, 4, FAKE, FAKE, pkv.BF16, FAKE, FAKE, ctypes.byref(_desc(block_size=8)),
+             None, None) == -3
+    assert f(FAKE, FAKE, 4, FAKE, 0, FAKE, FAKE, pkv.BF16, FAKE, FAKE, d, None, None) == -3  # no table row
+    assert f(FAKE, FAKE, -1, FAKE, 4, FAKE, FAKE, pkv.BF16, FAKE, FAKE, d, None, None) == -3
+    assert f(None, FAKE, 4, FAKE, 4, FAKE, FAKE, pkv.BF16, FAKE, FAKE, d, None, None) == -1
+    assert f(FAKE, None, 4, FAKE, 4, FAKE, FAKE, pkv.BF16, FAKE, FAKE, d, None, None) == -1
+    assert f(FAKE, FAKE, 4, None, 4, FAKE, FAKE, pkv.BF16, FAKE, FAKE, d, None, None) == -1
+    assert f(FAKE, FAKE, 4, FAKE, 4, None, FAKE, pkv.BF16, FAKE, FAKE, d, None, None) == -1
+    assert f(FAKE, FAKE, 4, FAKE, 4, FAKE, FAKE, pkv.BF16, FAKE, FAKE, None, None, None) == -1
+    assert f(None, None, 0, None, 4, None, None, pkv.BF16, None, None, d, None, None) == 0
+    misaligned = ctypes.c_void_p(0x100004)
+    assert f(FAKE, FAKE, 4, FAKE, 4, FAKE, FAKE, pkv.BF16, misaligned, FAKE, d, None, None) == -3
 
 
 def test_slot_mapping_argument_errors():

@@ -109,6 +109,39 @@ def test_slots_without_a_cache_row_skip(orc, kind):
     assert np.array_equal(cache_bytes(g.v_cache), before_v)
 
 
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_write_positions_matches_slots_then_write(orc, name):
+    """Slot resolution inside the write kernel: the caches come out bit-identical to the
+    oracle's slot mapping followed by its write, and the returned slots are the oracle's.
+    Tokens with no cache row (bad sequence ID or position) then write nothing."""
+    w = make_workload(SMALL[name])
+    g = GpuStep(w)
+    c = w.cfg
+    g.fill_history()
+    slots = torch.full((c.num_seqs,), 7, dtype=torch.int64, device="cuda")
+    pkv.paged_kv_write_positions(g.new_seq, g.new_pos, g.block_tables, g.new_k, g.new_v, g.k_cache, g.v_cache,
+                                 g.kv_dtype, w.k_scale, w.v_scale, slot_mapping=slots)
+    torch.cuda.synchronize()
+    kc, vc, ns, _ = oracle_step(orc, w, pairs=np.zeros((0, 2), np.int32))
+    assert np.array_equal(slots.cpu().numpy(), ns)
+    assert np.array_equal(cache_bytes(g.k_cache).reshape(-1), kc.view(np.uint8).reshape(-1))
+    assert np.array_equal(cache_bytes(g.v_cache).reshape(-1), vc.view(np.uint8).reshape(-1))
+    # no cache row: a negative sequence ID or position, a position past the table's row
+    nb = w.block_tables.shape[1]
+    bad_seq = torch.tensor([(-1, 0, 0)[i % 3] for i in range(c.num_seqs)], dtype=torch.int32, device="cuda")
+    bad_pos = torch.tensor([(5, -3, nb * c.block_size)[i % 3] for i in range(c.num_seqs)], dtype=torch.int32,
+                           device="cuda")
+    before_k, before_v = cache_bytes(g.k_cache).copy(), cache_bytes(g.v_cache).copy()
+    pkv.paged_kv_write_positions(bad_seq, bad_pos, g.block_tables, g.new_k, g.new_v, g.k_cache, g.v_cache,
+                                 g.kv_dtype, w.k_scale, w.v_scale, slot_mapping=slots)
+    pkv.paged_kv_write_positions(bad_seq, bad_pos, g.block_tables, g.new_k, g.new_v, g.k_cache, g.v_cache,
+                                 g.kv_dtype, w.k_scale, w.v_scale)  # no slot output
+    torch.cuda.synchronize()
+    assert np.all(slots.cpu().numpy() == -1)
+    assert np.array_equal(cache_bytes(g.k_cache), before_k)
+    assert np.array_equal(cache_bytes(g.v_cache), before_v)
+
+
 def test_slot_mapping_without_a_table_entry(orc):
     """A negative position or sequence ID, or a position whose block index is past the
     table's row, maps to -1; the other tokens map as the oracle does."""
