@@ -605,7 +605,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this path has "
-              "no multi-GPU leg; sharding is described in DESIGN.md", file=sys.stderr)
+              "no multi-GPU leg (a decode step shards by KV head or by sequence, with no collective "
+              "inside the step)", file=sys.stderr)
         sys.exit(2)
     clocks = gpu_clocks() if not args.copy_calibration and not args.prefill_only else None
     import torch

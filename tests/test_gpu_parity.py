@@ -14,7 +14,7 @@ from gpu_helpers import (GpuStep, assert_close_to_oracle, cache_bytes, out_to_f6
                          torch_dtype)
 from helpers import oracle_step
 from pins import SMALL
-from workloads import CONFIGS, LLAMA8B, R70B_FP8, TINY, make_workload
+from workloads import CONFIGS, LLAMA8B, LONGCTX, R70B_FP8, TINY, make_workload
 
 pytestmark = pytest.mark.gpu
 THREADS = min(16, len(os.sched_getaffinity(0)))
@@ -172,7 +172,7 @@ def test_decode_small(orc, name, mode):
     assert_close_to_oracle(out, ref, w.cfg.kv_dtype, f"{name}/{mode}")
 
 
-FULL_MODES = [(c, None) for c in CONFIGS] + [(CONFIGS[4], 0), (CONFIGS[1], 512)]
+FULL_MODES = [(c, None) for c in CONFIGS] + [(LONGCTX, 0), (LLAMA8B, 512)]
 
 
 @pytest.mark.parametrize("cfg,part", FULL_MODES,
