@@ -29,6 +29,26 @@ def test_library_exports_every_declared_symbol():
     assert pkv.pkv_abi_version() == 7
 
 
+def test_cache_desc_mirror_matches_the_c_layout(tmp_path):
+    """The ctypes mirror of pkv_cache_desc has the C struct's size and field offsets
+    (a small C program compiled against the header reports them)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in CacheDesc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include "pagedkv.h"\nint main(void) {\n'
+                   '  printf("%zu", sizeof(pkv_cache_desc));\n'
+                   + "".join(f'  printf(" %zu", offsetof(pkv_cache_desc, {f}));\n' for f in fields)
+                   + '  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{HEADER.parent}", "-I/opt/rocm/include", str(src),
+                    "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got == [ctypes.sizeof(CacheDesc)] + [getattr(CacheDesc, f).offset for f in fields]
+
+
 def test_workspace_header_constant_matches_header():
     m = re.search(r"#define\s+PKV_WORKSPACE_HEADER_BYTES\s+(\d+)", HEADER.read_text())
     assert m and int(m.group(1)) == pkv.WORKSPACE_HEADER_BYTES
