@@ -480,38 +480,44 @@ def measure_block_moves(args):
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def measure_prefill(args):
+def measure_prefill(args, kv="bf16"):
     """Chunked prefill: 8 sequences, each a 512-token chunk ending a 4096-token context
-    (Llama-3-8B-shaped heads, bf16).  Algorithmic flops: per query head and attended
-    (query, token) pair, 2 d for q.k and 2 d for p v; MFMA-bound."""
+    (Llama-3-8B-shaped heads, bf16 queries; a bf16 or an fp8 e4m3fn cache).  Algorithmic
+    flops: per query head and attended (query, token) pair, 2 d for q.k and 2 d for p v;
+    MFMA-bound (the fp8 tiles are converted to bf16 for bf16 MFMAs)."""
     import numpy as np
     import torch
     import paged_kv_cache_27_amd as pkv
     from workloads import LLAMA8B, POISON_BITS, cache_shape, make_workload, prefill_queries
 
-    cfg = LLAMA8B.replace(name="prefill-8x512-at-4096-bf16", num_seqs=8, ctx_kind="fixed",
-                          ctx_params=(4096,) * 8)
+    name = "prefill-8x512-at-4096-bf16" if kv == "bf16" else "prefill-8x512-at-4096-fp8kv"
+    cfg = LLAMA8B.replace(name=name, num_seqs=8, ctx_kind="fixed", ctx_params=(4096,) * 8, kv_dtype=kv)
     w = make_workload(cfg)
     c = cfg
     n = np.full(c.num_seqs, 512, np.int32)
     q_np, cu_np = prefill_queries(w, n)
     dev = "cuda"
-    k = torch.full(cache_shape(w), POISON_BITS["bf16"], dtype=torch.int16, device=dev).view(torch.bfloat16)
-    v = torch.full(cache_shape(w), POISON_BITS["bf16"], dtype=torch.int16, device=dev).view(torch.bfloat16)
+    store = torch.int16 if kv == "bf16" else torch.uint8
+    k = torch.full(cache_shape(w), POISON_BITS[kv], dtype=store, device=dev)
+    v = torch.full(cache_shape(w), POISON_BITS[kv], dtype=store, device=dev)
+    if kv == "bf16":
+        k, v = k.view(torch.bfloat16), v.view(torch.bfloat16)
+    kvd = None if kv == "bf16" else "fp8"
     bt = torch.from_numpy(w.block_tables).to(dev)
     ctx = torch.from_numpy(w.context_lens).to(dev)
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
     hs = torch.from_numpy(w.hist_seq).to(dev)
     hp = torch.from_numpy(w.hist_pos).to(dev)
     slots = pkv.paged_kv_slot_mapping(hs, hp, bt, c.block_size)
-    pkv.paged_kv_write(slots, up(w.hist_k), up(w.hist_v), k, v)
+    pkv.paged_kv_write(slots, up(w.hist_k), up(w.hist_v), k, v, kvd, w.k_scale, w.v_scale)
     ns = pkv.paged_kv_slot_mapping(torch.from_numpy(w.new_seq).to(dev), torch.from_numpy(w.new_pos).to(dev), bt,
                                    c.block_size)
-    pkv.paged_kv_write(ns, up(w.new_k), up(w.new_v), k, v)
+    pkv.paged_kv_write(ns, up(w.new_k), up(w.new_v), k, v, kvd, w.k_scale, w.v_scale)
     q = up(q_np)
     cu = torch.from_numpy(cu_np).to(dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    call = lambda: pkv.paged_attention_prefill(q, cu, 512, k, v, bt, ctx, w.scale, out, w.max_context_len)
+    call = lambda: pkv.paged_attention_prefill(q, cu, 512, k, v, bt, ctx, w.scale, out, w.max_context_len,
+                                               kv_dtype=kvd, k_scale=w.k_scale, v_scale=w.v_scale)
     for _ in range(3):
         call()
     flush = torch.ones(256 << 20, dtype=torch.float32, device=dev)
@@ -644,6 +650,7 @@ def main():
                 torch.cuda.empty_cache()
     blocks = measure_block_moves(args) if args.all else None
     prefill = measure_prefill(args) if args.all else None
+    prefill_fp8 = measure_prefill(args, "fp8") if args.all else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -683,7 +690,8 @@ def main():
     if args.json_out:
         Path(args.json_out).parent.mkdir(parents=True, exist_ok=True)
         Path(args.json_out).write_text(json.dumps({"headline": res, "others": others, "block_moves": blocks,
-                                                   "prefill": prefill, "cpu": cpu}, indent=1))
+                                                   "prefill": prefill, "prefill_fp8kv": prefill_fp8,
+                                                   "cpu": cpu}, indent=1))
     print(json.dumps(line), flush=True)
 
 
