@@ -8,14 +8,20 @@ the context is split).  Inputs are synthetic and
 seeded, resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout:
-  value        effective KV GB/s of the step = algorithmic bytes of a step / step time
+  value        effective KV GB/s of the step = algorithmic bytes of a step / step time,
+               on the headline workload (the Llama-3-8B-shaped layer unless --config)
   roofline     the decode call (its dominant kernel) against the 8 TB/s HBM peak: its
                average duration over back-to-back calls on 4 copies of the layer's cache
                taken in turn (each call reads cold data, as consecutive layers do), HIP
                events on the stream it runs on; single launches after an L2/MALL flush
-               are reported beside it
+               are reported beside it.  Bytes are the algorithmic bytes; where sequences
+               share blocks (prefix caching) the unique bytes, each shared block once
   read_ceiling the same tiles read by a streaming-read probe, timed the same way
   cpu_baseline the fp64 oracle timed on this host's cores on a bounded sample
+  configs      every one of the five decode-layer workloads measured the same way (the
+               headline's entry is the headline's measurement), each with its own
+               roofline fraction, read ceiling, single-launch percentiles and oracle
+               baseline; --only skips them
 """
 from __future__ import annotations
 
@@ -55,7 +61,12 @@ def parse_args():
     ap.add_argument("--config", default="llama3-8b-shaped-bf16-64seq",
                     help="workload name or 1-based index (default: the 8B-shaped layer)")
     ap.add_argument("--reps", type=int, default=30, help="cold-cache reps of the roofline leg (>= 1)")
-    ap.add_argument("--all", action="store_true", help="also measure every other workload (stderr + --json-out)")
+    ap.add_argument("--all", action="store_true",
+                    help="also the windowed workload, block moves and prefill (stderr + --json-out)")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the headline workload only (no configs array; e.g. under a profiler)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="wall budget of the oracle leg of each non-headline workload")
     ap.add_argument("--json-out", default=None, help="write per-workload results here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the oracle leg")
@@ -107,8 +118,16 @@ def algorithmic_bytes(w):
     write = n * hkv * d * 2 * (DT_BYTES[c.src_dtype] + DT_BYTES[c.kv_dtype])
     slots = n * (4 + 4 + 4)
     unique_kv = w.kv_bytes_unique()
-    return {"decode": decode, "kv": kv, "kv_unique": unique_kv, "write": write, "slots": slots,
-            "step": decode + write + slots}
+    return {"decode": decode, "kv": kv, "kv_unique": unique_kv, "decode_unique": decode - kv + unique_kv,
+            "write": write, "slots": slots, "step": decode + write + slots}
+
+
+def roofline_bytes(nbytes, w):
+    """Bytes of one decode call priced against HBM: each shared physical block once when
+    sequences share blocks (the logical bytes, every sequence's whole context, would count
+    a shared prefix once per sequence and could exceed the peak), else the algorithmic
+    bytes."""
+    return nbytes["decode_unique"] if w.shared_blocks else nbytes["decode"]
 
 
 class Step:
@@ -351,27 +370,30 @@ def read_ceiling(w, st, reps, copies):
             "ms_cold_mean": ms, "ms_layered": lay, "GBps": 2 * n * tb / (lay * 1e-3) / 1e9}
 
 
-def measure(cfg, args, partition=None):
+def measure(cfg, args, partition=None, steps=None, warmup=None):
     import numpy as np
     import torch
     from workloads import make_workload
 
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     t0 = time.time()
     w = make_workload(cfg)
     log(f"[{cfg.name}] inputs generated in {time.time() - t0:.1f}s")
     st = Step(w, partition if partition is not None else args.partition,
               shared_prefix=not args.no_shared_prefix)
     nbytes = algorithmic_bytes(w)
+    rbytes = roofline_bytes(nbytes, w)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         st.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         st.step()
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    ms_step = (t2 - t1) * 1e3 / args.steps
+    ms_step = (t2 - t1) * 1e3 / steps
 
     # Cold-cache leg: L2 and MALL flushed before each rep by reading 1 GiB (a read leaves
     # no dirty lines to write back during the timed call); HIP events on the stream the
@@ -403,7 +425,7 @@ def measure(cfg, args, partition=None):
         "write_ms_cold_mean": float(np.mean(t_write)),
         "decode_GBps_cold": achieved, "decode_frac_hbm_peak": achieved / HBM_PEAK_GBS,
         "decode_unique_GBps_cold": (nbytes["decode"] - nbytes["kv"] + nbytes["kv_unique"]) / (dec_ms * 1e-3) / 1e9,
-        "bytes": nbytes, "schedule": st.schedule,
+        "bytes": nbytes, "roofline_bytes": rbytes, "schedule": st.schedule,
         "max_context_len": w.max_context_len, "sum_context": int(w.context_lens.sum()),
     }
     # layered leg: LAYERS copies of this layer's cache decoded in turn, back to back
@@ -417,6 +439,7 @@ def measure(cfg, args, partition=None):
     st.k_cache, st.v_cache = k0, v0
     res["decode_ms_layered"] = lay_ms
     res["decode_GBps_layered"] = nbytes["decode"] / (lay_ms * 1e-3) / 1e9
+    res["roofline_GBps_layered"] = rbytes / (lay_ms * 1e-3) / 1e9
     ceil = read_ceiling(w, st, max(4, args.reps // LAYERS), copies)
     del copies
     torch.cuda.empty_cache()
@@ -425,10 +448,10 @@ def measure(cfg, args, partition=None):
     ceil["decode_frac"] = ceil["ms_layered"] / lay_ms
     res["read_ceiling"] = ceil
     log(f"[{cfg.name}] step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s), decode cold "
-        f"{dec_ms * 1e3:.1f} us ({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak), "
+        f"{dec_ms * 1e3:.1f} us ({achieved:.0f} GB/s), "
         f"write {res['write_ms_cold_mean'] * 1e3:.1f} us, schedule {res['schedule']}; layered decode "
-        f"{lay_ms * 1e3:.1f} us ({res['decode_GBps_layered']:.0f} GB/s, "
-        f"{100 * res['decode_GBps_layered'] / HBM_PEAK_GBS:.1f}%); read ceiling of its tiles "
+        f"{lay_ms * 1e3:.1f} us ({res['decode_GBps_layered']:.0f} GB/s; roofline "
+        f"{100 * res['roofline_GBps_layered'] / HBM_PEAK_GBS:.1f}% of peak); read ceiling of its tiles "
         f"{ceil['GBps']:.0f} GB/s ({ceil['ms_layered'] * 1e3:.1f} us layered), decode at "
         f"{100 * ceil['decode_frac']:.1f}% of it")
     return w, st, res
@@ -454,11 +477,16 @@ def measure_block_moves(args):
     dst = torch.from_numpy(perm[n:2 * n].copy()).cuda()
     kb = torch.empty((n,) + tuple(shape[1:]), dtype=torch.bfloat16, device="cuda")
     vb = torch.empty_like(kb)
+    # pinned host buffers: the swap kernel itself moves the blocks across the host link
+    kh = torch.empty((n,) + tuple(shape[1:]), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty((n,) + tuple(shape[1:]), dtype=torch.bfloat16, pin_memory=True)
     flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
     out = {}
     for name, call in (("copy_blocks", lambda: pkv.paged_kv_copy_blocks(src, dst, k, v)),
-                       ("swap_out_to_device", lambda: pkv.paged_kv_swap_out(src, k, v, kb, vb))):
+                       ("swap_out_to_device", lambda: pkv.paged_kv_swap_out(src, k, v, kb, vb)),
+                       ("swap_out_to_pinned_host", lambda: pkv.paged_kv_swap_out(src, k, v, kh, vh)),
+                       ("swap_in_from_pinned_host", lambda: pkv.paged_kv_swap_in(dst, kh, vh, k, v))):
         for _ in range(3):
             call()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.reps)]
@@ -469,6 +497,13 @@ def measure_block_moves(args):
             e1.record()
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        if "host" in name:  # one direction across the host link: K and V blocks
+            nbytes = n * block_bytes * 2
+            out[name] = {"blocks": n, "block_bytes": block_bytes, "bytes_over_link": nbytes, "ms_cold_mean": ms,
+                         "GBps_link": nbytes / (ms * 1e-3) / 1e9}
+            log(f"[block moves] {name}: {n} blocks of {block_bytes} B (K and V), {ms * 1e3:.1f} us, "
+                f"{out[name]['GBps_link']:.1f} GB/s across the host link")
+            continue
         nbytes = n * block_bytes * 2 * 2
         out[name] = {"blocks": n, "block_bytes": block_bytes, "bytes": nbytes, "ms_cold_mean": ms,
                      "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -540,10 +575,26 @@ def measure_prefill(args, kv="bf16"):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        for ln in Path("/proc/cpuinfo").read_text().splitlines():
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# Oracle threads: the host CPUs this process may run on, at most the 16 a one-GPU box's
+# share holds (its affinity mask can list more CPUs than the share).
+CPU_SHARE = 16
+
+
 def cpu_baseline(w, budget_s):
-    """The fp64 oracle on this host's cores (up to 16 threads) over whole sequences (all
-    query heads), taken in order until the wall budget is spent; then the same on one
-    thread for a third of the budget (`single_thread`)."""
+    """The fp64 oracle on this host's cores (its affinity, at most CPU_SHARE threads) over
+    whole sequences (all query heads), taken in order until the wall budget is spent; then
+    the same on one thread for a third of the budget (`single_thread`)."""
     import numpy as np
     from oracle.oracle import Oracle
     from workloads import poisoned_cache
@@ -555,10 +606,14 @@ def cpu_baseline(w, budget_s):
     orc.kv_write(hs, w.hist_k, w.hist_v, c.src_dtype, kc, vc, c.kv_dtype, w.k_scale, w.v_scale)
     ns = orc.slot_mapping(w.new_seq, w.new_pos, w.block_tables, c.block_size)
     orc.kv_write(ns, w.new_k, w.new_v, c.src_dtype, kc, vc, c.kv_dtype, w.k_scale, w.v_scale)
-    threads = min(16, len(os.sched_getaffinity(0)))
+    affinity = len(os.sched_getaffinity(0))
+    threads = min(CPU_SHARE, affinity)
     res = _oracle_rate(orc, w, kc, vc, threads, budget_s)
     one = _oracle_rate(orc, w, kc, vc, 1, budget_s / 3)
     res["single_thread"] = {"value": one["value"], "unit": "GB/s", "cores": 1, "sample": one["sample"]}
+    res["affinity_cpus"] = affinity
+    res["cpu_model"] = cpu_model()
+    res["threads_note"] = f"threads = min(affinity {affinity}, the box's {CPU_SHARE}-CPU share)"
     return res
 
 
@@ -590,6 +645,42 @@ def _oracle_rate(orc, w, kc, vc, threads, budget_s):
             "sample": f"{passes:.2f} passes of the decode over all {c.num_seqs} sequences x "
                       f"{c.num_q_heads} query heads ({tokens} context tokens in total), fp64, "
                       f"{elapsed:.1f}s wall on {threads} threads"}
+
+
+def config_entry(res, cpu):
+    """One workload's entry of the `configs` array: the decode call against the HBM
+    roofline (layered mean), its single-launch percentiles, HBM traffic, read ceiling and
+    the oracle's rate on this host."""
+    r = lambda x, n=2: None if x is None else round(x, n)
+    rb, logical = res["roofline_bytes"], res["bytes"]["decode"]
+    ceil = res["read_ceiling"]
+    e = {"workload": res["workload"], "schedule": res["schedule"],
+         "kernel": kernel_label(res["schedule"]),
+         "decode_us_layered": r(res["decode_ms_layered"] * 1e3),
+         "bytes_per_launch": rb,
+         "bytes_basis": "unique (each shared block once)" if rb != logical else "algorithmic",
+         "GBps": r(res["roofline_GBps_layered"], 1),
+         "frac_hbm_peak": r(res["roofline_GBps_layered"] / HBM_PEAK_GBS, 4),
+         "decode_us_single_launch": {"mean": r(res["decode_ms_cold_mean"] * 1e3),
+                                     "p10": r(res["decode_ms_cold_p10"] * 1e3),
+                                     "median": r(res["decode_ms_cold_median"] * 1e3),
+                                     "p90": r(res["decode_ms_cold_p90"] * 1e3)},
+         "traffic": traffic_for(res["workload"]),
+         "read_ceiling": {"us_layered": r(ceil["ms_layered"] * 1e3), "GBps": r(ceil["GBps"], 1),
+                          "decode_frac": r(ceil["decode_frac"], 4)},
+         "step_us": r(res["ms_per_step"] * 1e3), "write_us_single_launch": r(res["write_ms_cold_mean"] * 1e3),
+         "seq_heads_per_s": r(res["seq_heads_per_s"], 1),
+         "cpu_baseline": None if cpu is None else {
+             "value": r(cpu["value"], 4), "unit": cpu["unit"], "cores": cpu["cores"], "kind": cpu["kind"],
+             "single_thread_value": r(cpu["single_thread"]["value"], 4), "affinity_cpus": cpu["affinity_cpus"],
+             "cpu_model": cpu["cpu_model"], "sample": cpu["sample"]}}
+    if rb != logical:  # prefix sharing: the logical bytes (every sequence's whole context) too
+        e["logical_bytes"] = logical
+        e["GBps_logical"] = r(res["decode_GBps_layered"], 1)
+        e["frac_logical"] = r(res["decode_GBps_layered"] / HBM_PEAK_GBS, 4)
+    if res["bytes"]["decode"] < 1 << 20:
+        e["note"] = "parity-only size: its whole budget at 6 TB/s is far below a launch's latency"
+    return e
 
 
 def gpu_clocks():
@@ -635,27 +726,44 @@ def main():
     if args.prefill_only:
         print(json.dumps(measure_prefill(args)))
         return
+    from workloads import CONFIGS, EXTRA_CONFIGS
     cfg = pick_config(args.config)
     w, st, res = measure(cfg, args)
     del st
     torch.cuda.empty_cache()
-    others = []
-    if args.all:
-        from workloads import CONFIGS, EXTRA_CONFIGS
-        for c in CONFIGS + EXTRA_CONFIGS:
-            if c.name != cfg.name:
-                _, s2, r2 = measure(c, args)
-                others.append(r2)
-                del s2
-                torch.cuda.empty_cache()
-    blocks = measure_block_moves(args) if args.all else None
-    prefill = measure_prefill(args) if args.all else None
-    prefill_fp8 = measure_prefill(args, "fp8") if args.all else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
         log(f"[cpu oracle] {cpu['value']:.3f} GB/s on {cpu['cores']} threads: {cpu['sample']}; "
             f"{cpu['single_thread']['value']:.3f} GB/s on one thread")
+    del w
+    # every decode-layer workload, measured the same way (the headline's entry is its own
+    # measurement); fewer steps, a smaller oracle budget
+    configs = []
+    if not args.only:
+        for c2 in CONFIGS:
+            if c2.name == cfg.name:
+                configs.append(config_entry(res, cpu))
+                continue
+            w2, s2, r2 = measure(c2, args, steps=min(args.steps, 20), warmup=min(args.warmup, 5))
+            del s2
+            torch.cuda.empty_cache()
+            cpu2 = None
+            if not args.no_cpu_baseline:
+                cpu2 = cpu_baseline(w2, args.config_cpu_seconds)
+                log(f"[cpu oracle, {c2.name}] {cpu2['value']:.3f} GB/s on {cpu2['cores']} threads")
+            del w2
+            configs.append(config_entry(r2, cpu2))
+    others = []
+    if args.all:
+        for c in EXTRA_CONFIGS:
+            _, s2, r2 = measure(c, args)
+            others.append(r2)
+            del s2
+            torch.cuda.empty_cache()
+    blocks = measure_block_moves(args) if args.all else None
+    prefill = measure_prefill(args) if args.all else None
+    prefill_fp8 = measure_prefill(args, "fp8") if args.all else None
     traffic = traffic_for(cfg.name)
     c = cfg
     line = {
@@ -673,11 +781,11 @@ def main():
         "seq_heads_per_s": round(res["seq_heads_per_s"], 1),
         # achieved: the decode call's average duration over back-to-back calls on cold
         # per-layer cache copies (the layered leg); the single-launch figure beside it
-        "roofline": {"bound": "hbm", "achieved": round(res["decode_GBps_layered"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(res["roofline_GBps_layered"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(res["decode_GBps_layered"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac": round(res["roofline_GBps_layered"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": kernel_label(res["schedule"]),
-                     "bytes_per_launch": res["bytes"]["decode"],
+                     "bytes_per_launch": res["roofline_bytes"],
                      "mean_launch_ms": round(res["decode_ms_layered"], 6),
                      "timing": f"mean over back-to-back calls on {LAYERS} cold per-layer cache copies",
                      "single_launch_ms": round(res["decode_ms_cold_mean"], 6),
@@ -685,11 +793,13 @@ def main():
         "cpu_baseline": cpu,
         "read_ceiling": {k: (round(v, 4) if isinstance(v, float) else v)
                          for k, v in res["read_ceiling"].items()},
+        "configs": configs,
         "env": env,
     }
     if args.json_out:
         Path(args.json_out).parent.mkdir(parents=True, exist_ok=True)
-        Path(args.json_out).write_text(json.dumps({"headline": res, "others": others, "block_moves": blocks,
+        Path(args.json_out).write_text(json.dumps({"headline": res, "configs": configs, "others": others,
+                                                   "block_moves": blocks,
                                                    "prefill": prefill, "prefill_fp8kv": prefill_fp8,
                                                    "cpu": cpu}, indent=1))
     print(json.dumps(line), flush=True)

@@ -70,7 +70,7 @@ typedef enum {
 /* pkv_cache_desc.flags: the block tables of one decode call may map several
  * sequences to the same physical block (prefix caching: "La despensa por
  * casilleros", section "Prefix caching"; "PagedAttention por dentro...", section
- * "Compartir prefijos").  The decode then reads K/V with the ordinary cache policy,
+ * "Prefix caching cross-session").  The decode then reads K/V with the ordinary cache policy,
  * so a shared block stays in L2 for its other readers.  Without the flag every
  * K/V byte is assumed to be read once per call and is read with the streaming
  * (nontemporal) policy, which is faster for such data.  Either way the results are
@@ -232,7 +232,7 @@ int paged_attention_decode_window(const void* q, pkv_dtype q_dtype, int32_t num_
  * Decode attention for a batch in which groups of sequences share a prefix of physical
  * blocks -- prefix caching: their block tables point at the same refcounted blocks
  * ("La despensa por casilleros", section "Prefix caching: compartir casilleros con
- * copy-on-write"; "PagedAttention por dentro...", section "Compartir prefijos").
+ * copy-on-write"; "PagedAttention por dentro...", section "Prefix caching cross-session").
  * Computes exactly what paged_attention_decode computes (same contract for every
  * argument it shares with it), reading each group's shared prefix once for the whole
  * group instead of once per sequence: the queries of the group's sequences are stacked
@@ -321,7 +321,10 @@ int paged_kv_copy_blocks(const int32_t* src_ids, const int32_t* dst_ids, int32_t
  * swap in: row i -> block ids[i].  ("PagedAttention por dentro...", section
  * "Estrategia 2: swap": an evicted session's blocks move to CPU RAM and back to VRAM
  * when it resumes.)  The buffers may be device memory or pinned host memory
- * (hipHostMalloc); 16-byte aligned.  Release the swapped-out blocks to the pool only
+ * (hipHostMalloc, e.g. torch's pin_memory), in which case the kernel moves the blocks
+ * across the host link itself; 16-byte aligned.  A buffer the HIP runtime does not know
+ * as device or pinned memory (pageable host memory) returns PKV_ERR_SHAPE before any
+ * launch.  Release the swapped-out blocks to the pool only
  * after the stream has finished the swap out, and decode from swapped-in blocks only
  * on the same stream after the swap in (or after synchronising with it).
  */

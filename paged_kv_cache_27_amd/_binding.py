@@ -144,6 +144,16 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr()
 
 
+def _buf_ptr(t: torch.Tensor) -> int:
+    """A swap buffer: a device tensor or a pinned host tensor (the library moves blocks
+    across the host link itself); pageable host memory is refused."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError("swap buffers must be device tensors or pinned host tensors (pin_memory=True)")
+    if not t.is_contiguous():
+        raise ValueError("tensors handed to the HIP library must be contiguous")
+    return t.data_ptr()
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -267,23 +277,24 @@ def paged_kv_copy_blocks(src_ids: torch.Tensor, dst_ids: torch.Tensor, k_cache: 
 
 def paged_kv_swap_out(ids: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       k_buf: torch.Tensor, v_buf: torch.Tensor, kv_dtype=None, stream=None) -> None:
-    """Blocks ids[i] of each cache -> row i of the device buffers ([n][block elements])."""
+    """Blocks ids[i] of each cache -> row i of the buffers ([n][block elements]), which may
+    be device tensors or pinned host tensors."""
     lib = load_library()
     desc = cache_desc(k_cache, kv_dtype)
     assert ids.dtype == torch.int32
     _check("paged_kv_swap_out",
            lib.paged_kv_swap_out(_ptr(ids), ids.numel(), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
-                                 _ptr(k_buf), _ptr(v_buf), _stream(stream)))
+                                 _buf_ptr(k_buf), _buf_ptr(v_buf), _stream(stream)))
 
 
 def paged_kv_swap_in(ids: torch.Tensor, k_buf: torch.Tensor, v_buf: torch.Tensor, k_cache: torch.Tensor,
                      v_cache: torch.Tensor, kv_dtype=None, stream=None) -> None:
-    """Row i of the device buffers -> blocks ids[i] of each cache."""
+    """Row i of the buffers (device or pinned host tensors) -> blocks ids[i] of each cache."""
     lib = load_library()
     desc = cache_desc(k_cache, kv_dtype)
     assert ids.dtype == torch.int32
     _check("paged_kv_swap_in",
-           lib.paged_kv_swap_in(_ptr(ids), ids.numel(), _ptr(k_buf), _ptr(v_buf), _ptr(k_cache),
+           lib.paged_kv_swap_in(_ptr(ids), ids.numel(), _buf_ptr(k_buf), _buf_ptr(v_buf), _ptr(k_cache),
                                 _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
 
 

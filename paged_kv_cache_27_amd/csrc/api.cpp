@@ -159,6 +159,29 @@ int check_write(int32_t num_tokens, const void* k, const void* v, int src_dtype,
   return PKV_OK;
 }
 
+// The address a kernel uses for a swap buffer: device memory as it is; pinned host
+// memory (hipHostMalloc, which maps it into every GPU's address space) through the
+// device address the runtime mapped for it.  Anything else -- pageable host memory, an
+// address the runtime does not know -- is refused (non-zero), since a kernel touching it
+// would fault.
+int device_view(void* p, void** out) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    if (!at.devicePointer) return -1;
+    *out = at.devicePointer;
+    return 0;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged || at.type == hipMemoryTypeUnified) {
+    *out = p;
+    return 0;
+  }
+  return -1;
+}
+
 // Write arguments without a slot source (the caller sets one).
 pkv::WriteArgs write_args(int32_t num_tokens, const void* k, const void* v, int src_dtype, void* k_cache,
                           void* v_cache, const pkv_cache_desc* cache) {
@@ -216,6 +239,77 @@ pkv::RowsArgs rows_args(const void* q, int q_dtype, int32_t num_seqs, int32_t nu
   p.out = nullptr;
   p.out_dtype = 0;
   return p;
+}
+
+
+// Checks of a decode call's arguments shared by the decode entry points (everything but
+// the workspace).
+int check_decode_call(const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                      const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                      int32_t window, int32_t sinks, const void* out, int out_dtype) {
+  int st = check_decode_shape(cache, q_dtype, out_dtype, num_seqs, num_q_heads, max_context_len);
+  if (st) return st;
+  if (window < 0 || sinks < 0) return PKV_ERR_SHAPE;
+  if (max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+// Launch a checked and planned decode; `workspace` holds plan.ws_bytes (unused when 0).
+int run_decode(const Plan& plan, const void* q, int q_dtype, int32_t num_seqs, int32_t num_q_heads,
+               const void* k_cache, const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, int32_t window,
+               int32_t sinks, float scale, void* out, int out_dtype, void* workspace, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.cache_dtype = cache->dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.kv_stream = kv_stream(cache) ? 1 : 0;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.window = window;
+  a.sinks = window > 0 ? sinks : 0;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.partition = plan.partition;
+  a.num_partitions = plan.parts;
+  a.ws_m = a.ws_l = a.ws_acc = nullptr;
+  a.sk_workers = plan.workers;
+  a.sk_count = nullptr;
+  a.sk_part = nullptr;
+  a.seq_begin = nullptr;
+  a.pre_part = nullptr;
+  a.pre_splits = 0;
+  char* body = (char*)workspace + pkv::kWsHeaderBytes;  // only used when ws_bytes > 0
+  if (plan.mode == kFixed) {
+    const size_t ml = pkv::ws_ml_bytes(num_seqs, num_q_heads, plan.parts);
+    a.ws_m = (float*)body;
+    a.ws_l = (float*)(body + ml);
+    a.ws_acc = (float*)(body + 2 * ml);
+  } else if (plan.mode == kBalanced) {
+    a.sk_count = (int32_t*)workspace;
+    a.sk_part = (float*)body;
+  }
+  hipError_t e = plan.mode == kBalanced ? pkv::launch_decode_streamk(a, stream)
+                                        : pkv::launch_decode(a, stream);
+  if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -303,7 +397,9 @@ int paged_kv_swap_out(const int32_t* ids, int32_t num, const void* k_cache, cons
   if (!ids || !k_cache || !v_cache || !k_buf || !v_buf) return PKV_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
     return PKV_ERR_SHAPE;
-  hipError_t e = pkv::launch_move_blocks(k_cache, v_cache, ids, k_buf, v_buf, nullptr, num,
+  void *kd, *vd;
+  if (device_view(k_buf, &kd) || device_view(v_buf, &vd)) return PKV_ERR_SHAPE;
+  hipError_t e = pkv::launch_move_blocks(k_cache, v_cache, ids, kd, vd, nullptr, num,
                                          block_bytes(cache), cache->num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
@@ -317,7 +413,10 @@ int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const v
   if (!ids || !k_cache || !v_cache || !k_buf || !v_buf) return PKV_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
     return PKV_ERR_SHAPE;
-  hipError_t e = pkv::launch_move_blocks(k_buf, v_buf, nullptr, k_cache, v_cache, ids, num,
+  void *kd, *vd;
+  if (device_view(const_cast<void*>(k_buf), &kd) || device_view(const_cast<void*>(v_buf), &vd))
+    return PKV_ERR_SHAPE;
+  hipError_t e = pkv::launch_move_blocks(kd, vd, nullptr, k_cache, v_cache, ids, num,
                                          block_bytes(cache), cache->num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
@@ -367,15 +466,10 @@ int paged_attention_decode_window(const void* q, pkv_dtype q_dtype, int32_t num_
                                   int32_t max_context_len, int32_t window, int32_t sinks, float scale,
                                   void* out, pkv_dtype out_dtype, int32_t partition_size,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = check_decode_shape(cache, q_dtype, out_dtype, num_seqs, num_q_heads, max_context_len);
-  if (st) return st;
-  if (window < 0 || sinks < 0) return PKV_ERR_SHAPE;
-  if (max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
-  if (num_seqs == 0) return PKV_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
-
+  int st = check_decode_call(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                             max_blocks_per_seq, context_lens, max_context_len, window, sinks, out,
+                             out_dtype);
+  if (st || num_seqs == 0) return st;
   Plan plan;
   st = plan_decode(cache, q_dtype, num_seqs, num_q_heads, max_context_len, partition_size, &plan);
   if (st) return st;
@@ -383,53 +477,9 @@ int paged_attention_decode_window(const void* q, pkv_dtype q_dtype, int32_t num_
     if (!workspace) return PKV_ERR_NULL;
     if (workspace_bytes < plan.ws_bytes || ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
   }
-
-  pkv::DecodeArgs a;
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.head_dim = cache->head_dim;
-  a.block_size = cache->block_size;
-  a.cache_dtype = cache->dtype;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.k_scale = cache->k_scale;
-  a.v_scale = cache->v_scale;
-  a.kv_stream = kv_stream(cache) ? 1 : 0;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.max_context_len = max_context_len;
-  a.scale = scale;
-  a.window = window;
-  a.sinks = window > 0 ? sinks : 0;
-  a.out = out;
-  a.out_dtype = out_dtype;
-  a.partition = plan.partition;
-  a.num_partitions = plan.parts;
-  a.ws_m = a.ws_l = a.ws_acc = nullptr;
-  a.sk_workers = plan.workers;
-  a.sk_count = nullptr;
-  a.sk_part = nullptr;
-  a.seq_begin = nullptr;
-  a.pre_part = nullptr;
-  a.pre_splits = 0;
-  char* body = (char*)workspace + pkv::kWsHeaderBytes;  // only used when ws_bytes > 0
-  if (plan.mode == kFixed) {
-    const size_t ml = pkv::ws_ml_bytes(num_seqs, num_q_heads, plan.parts);
-    a.ws_m = (float*)body;
-    a.ws_l = (float*)(body + ml);
-    a.ws_acc = (float*)(body + 2 * ml);
-  } else if (plan.mode == kBalanced) {
-    a.sk_count = (int32_t*)workspace;
-    a.sk_part = (float*)body;
-  }
-  hipError_t e = plan.mode == kBalanced ? pkv::launch_decode_streamk(a, stream)
-                                        : pkv::launch_decode(a, stream);
-  if (e == hipErrorInvalidValue) return PKV_ERR_SHAPE;
-  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+  return run_decode(plan, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                    max_blocks_per_seq, context_lens, max_context_len, window, sinks, scale, out, out_dtype,
+                    workspace, stream);
 }
 
 size_t paged_attention_shared_prefix_workspace_size(const pkv_cache_desc* cache, pkv_dtype q_dtype,

@@ -619,11 +619,23 @@ struct MfmaDecoder {
       }
     }
     // ---- P.V
+    // A chunk holding tokens between the sinks and the window start (wave-uniform test:
+    // only the chunks at those two edges): their weights are zero, but a zero weight
+    // times a non-finite V element is NaN on the matrix cores, and the definition leaves
+    // those tokens out entirely, so their V fragments are replaced by zeros.
+    const bool gap = win_lo > sink_hi && ct < win_lo && ct + 16 > sink_hi;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       typename P::frag vf[HALVES];
 #pragma unroll
       for (int hf = 0; hf < HALVES; ++hf) vf[hf] = P::vfrag(buf.v[k], hf);
+      if (gap) {
+        const int t = tb + 4 * k;
+        if (t >= sink_hi && t < win_lo) {
+#pragma unroll
+          for (int hf = 0; hf < HALVES; ++hf) vf[hf] = typename P::frag{};
+        }
+      }
 #pragma unroll
       for (int hs = 0; hs < HS; ++hs) {
         typename P::frag ahi, alo;

@@ -4,7 +4,7 @@
 // Shared-prefix decode (the prefix half of cascade attention).  With prefix caching
 // several sequences map their first blocks to the same physical blocks ("La despensa
 // por casilleros", section "Prefix caching: compartir casilleros con copy-on-write";
-// "PagedAttention por dentro...", section "Compartir prefijos").  Attention over those
+// "PagedAttention por dentro...", section "Prefix caching cross-session").  Attention over those
 // shared tokens is the same matrix product for every sequence of the group, so it is
 // computed once for all of them: the queries of the group's sequences (for one KV head:
 // n_seqs x G rows) are the rows of S = Q K^T, P = online-softmax(S), O = P V over the

@@ -55,8 +55,8 @@ def test_workspace_header_constant_matches_header():
 
 
 def test_status_strings():
-    for code in range(0, -7, -1):
-        assert pkv.pkv_status_string(code)
+    for code in range(0, -9, -1):
+        assert pkv.pkv_status_string(code) != "unknown status"
     assert pkv.pkv_status_string(-99) == "unknown status"
 
 

@@ -76,31 +76,58 @@ def test_copy_blocks_bit_exact(orc, cfg):
     _assert_caches_equal(g, kc, vc, "copy_blocks")
 
 
-def test_swap_round_trip_through_pinned_host_memory(orc):
-    w, g, kc, vc = _prepared(orc, LLAMA8B.replace(num_seqs=2, ctx_params=(64, 200), pool_factor=3.0))
+SWAP_CASES = [("bf16", "device"), ("bf16", "pinned-host"), ("fp8", "pinned-host")]
+
+
+@pytest.mark.parametrize("kv,where", SWAP_CASES, ids=[f"{k}-{w}" for k, w in SWAP_CASES])
+def test_swap_round_trip(orc, kv, where):
+    """Swap out to buffers in device memory or straight to pinned host memory (the kernel
+    moves the blocks across the host link: "Estrategia 2: swap" keeps an evicted session
+    in CPU RAM), byte-compared with the oracle's swap-out; then swap in from the same
+    buffers to other blocks, caches compared byte for byte."""
+    base = LLAMA8B if kv == "bf16" else R70B_FP8.replace(ctx_params=(100, 0.5, 16, 300))
+    cfg = base.replace(num_seqs=2, pool_factor=3.0) if kv == "fp8" else \
+        base.replace(num_seqs=2, ctx_params=(64, 200), pool_factor=3.0)
+    w, g, kc, vc = _prepared(orc, cfg)
     live = _live_blocks(w)
     free = [b for b in range(w.num_blocks) if b not in set(live)]
     ids = np.array(live[:5] + [-1, w.num_blocks], np.int32)  # the last two rows skipped
     shape = (ids.size,) + tuple(g.k_cache.shape[1:])
-    kb = torch.zeros(shape, dtype=g.k_cache.dtype, device="cuda")
-    vb = torch.zeros_like(kb)
+    if where == "device":
+        kb = torch.zeros(shape, dtype=g.k_cache.dtype, device="cuda")
+        vb = torch.zeros_like(kb)
+    else:
+        kb = torch.zeros(shape, dtype=g.k_cache.dtype, pin_memory=True)
+        vb = torch.zeros(shape, dtype=g.k_cache.dtype, pin_memory=True)
+        assert kb.is_pinned() and vb.is_pinned()
+    print(f"swap case {kv} {where}: {ids.size} rows", flush=True)
     pkv.paged_kv_swap_out(_ids(ids), g.k_cache, g.v_cache, kb, vb, g.kv_dtype)
-    k_ref, v_ref = orc.swap_out(np.where(ids < w.num_blocks, ids, -1), kc, vc)
     torch.cuda.synchronize()
+    k_ref, v_ref = orc.swap_out(np.where(ids < w.num_blocks, ids, -1), kc, vc)
     assert np.array_equal(cache_bytes(kb)[:5], k_ref.view(np.uint8)[:5])
     assert np.array_equal(cache_bytes(vb)[:5], v_ref.view(np.uint8)[:5])
-    # to pinned host memory and back (the transfer of the swap)
-    kh = torch.empty(shape, dtype=kb.dtype, pin_memory=True)
-    vh = torch.empty(shape, dtype=kb.dtype, pin_memory=True)
-    kh.copy_(kb, non_blocking=True)
-    vh.copy_(vb, non_blocking=True)
-    torch.cuda.synchronize()
-    kb2, vb2 = kh.cuda(), vh.cuda()
+    assert not cache_bytes(kb)[5:].any() and not cache_bytes(vb)[5:].any()  # skipped rows untouched
     back = np.array(free[:5] + [w.num_blocks + 3, -1], np.int32)
-    pkv.paged_kv_swap_in(_ids(back), kb2, vb2, g.k_cache, g.v_cache, g.kv_dtype)
+    pkv.paged_kv_swap_in(_ids(back), kb, vb, g.k_cache, g.v_cache, g.kv_dtype)
     torch.cuda.synchronize()
     orc.swap_in(np.where(back < w.num_blocks, back, -1), k_ref, v_ref, kc, vc)
     _assert_caches_equal(g, kc, vc, "swap_in")
+
+
+def test_swap_refuses_pageable_host_memory():
+    """A pageable host buffer is refused before any launch (a kernel would fault on it)."""
+    cfg = LLAMA8B.replace(num_seqs=1, ctx_kind="fixed", ctx_params=(40,), pool_blocks=8)
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    kb = torch.zeros((1,) + tuple(g.k_cache.shape[1:]), dtype=g.k_cache.dtype)  # pageable
+    lib = pkv.load_library()
+    import ctypes
+    desc = pkv.cache_desc(g.k_cache)
+    rc = lib.paged_kv_swap_out(_ids([0]).data_ptr(), 1, g.k_cache.data_ptr(), g.v_cache.data_ptr(),
+                               ctypes.byref(desc), kb.data_ptr(), kb.data_ptr(), None)
+    assert rc == -3
+    with pytest.raises(ValueError):
+        pkv.paged_kv_swap_out(_ids([0]), g.k_cache, g.v_cache, kb, kb)
 
 
 def test_beam_fork_copy_on_write_then_decode(orc):

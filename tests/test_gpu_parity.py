@@ -286,6 +286,9 @@ EDGE = {
                                  ctx_params=(0, 1, 300, 0, 17, 1000, 16, 2, 4097, 33)),
     "many-seqs-short": LLAMA8B.replace(num_seqs=600, num_q_heads=8, num_kv_heads=2,
                                        ctx_params=(1, 40)),
+    # 1100 sequences x 8 KV heads: many short contexts, every schedule
+    "many-pairs-fixed": LLAMA8B.replace(num_seqs=1100, num_q_heads=8, num_kv_heads=8,
+                                        ctx_params=(1, 90)),
 }
 
 

@@ -13,7 +13,7 @@ import torch
 
 import paged_kv_cache_27_amd as pkv
 from gpu_helpers import GpuStep, assert_close_to_oracle, out_to_f64
-from helpers import free_blocks_outside_window, oracle_step
+from helpers import attended_tokens, free_blocks_outside_window, oracle_step
 from pins import SMALL, WINDOW_CASES
 from workloads import LONGCTX, R70B_FP8, make_workload
 
@@ -118,3 +118,64 @@ def test_window_full_size(orc, cfg, window, sinks, part):
     kc, vc, _, _ = oracle_step(orc, w, pairs=np.zeros((0, 2), np.int32))
     ref = _oracle_window(orc, w, kc, vc, window, sinks, bt)
     assert_close_to_oracle(out, ref, w.cfg.kv_dtype, cfg.name)
+
+
+NONFINITE = {"bf16": (0x7FC0, 0x7F80, 0xFF80), "fp8": (0x7F, 0xFF)}  # NaN, +inf, -inf / NaN codes
+
+
+def _poison_unattended(w, g, kc, vc, window, sinks, bt):
+    """Write NaN and infinities into K and V (every KV head) of each written token the
+    window leaves out whose block is still in use (it also holds attended tokens): data
+    the definition excludes, which a decode must not let in through a zero weight."""
+    c = w.cfg
+    B, codes = c.block_size, NONFINITE[c.kv_dtype]
+    kg = g.k_cache.view(torch.int16 if c.kv_dtype == "bf16" else torch.uint8)
+    vg = g.v_cache.view(torch.int16 if c.kv_dtype == "bf16" else torch.uint8)
+    kh, vh = kc.view(np.uint16 if c.kv_dtype == "bf16" else np.uint8), vc.view(np.uint16 if c.kv_dtype == "bf16" else np.uint8)
+    # rows (physical block, offset) some sequence attends, and the blocks holding them (a
+    # block may be shared between sequences: a row any of them attends stays finite)
+    attended, live = set(), set()
+    for s, ctx in enumerate(w.context_lens.tolist()):
+        for t in attended_tokens(ctx, window, sinks).tolist():
+            attended.add((int(bt[s, t // B]), t % B))
+            live.add(int(bt[s, t // B]))
+    n, done = 0, set()
+    for s, ctx in enumerate(w.context_lens.tolist()):
+        for t in range(ctx):
+            blk, off = int(bt[s, t // B]), t % B
+            if blk not in live or (blk, off) in attended or (blk, off) in done:
+                continue
+            done.add((blk, off))
+            code = codes[n % len(codes)]
+            n += 1
+            signed = code - 0x10000 if c.kv_dtype == "bf16" and code >= 0x8000 else code
+            for dst, host in ((kg, kh), (vg, vh)):
+                dst[blk, :, off, :] = signed
+                host[blk, :, off, :] = code
+    return n
+
+
+WINDOW_NONFINITE = [("ragged", 15, 0), ("ragged", 17, 15), ("ragged", 31, 16), ("ragged", 20, 33),
+                    ("ragged", 10, 3), ("ragged", 2, 40), ("prefix", 40, 4), ("r70b", 20, 4), ("r70b", 9, 2)]
+
+
+@pytest.mark.parametrize("name,window,sinks", WINDOW_NONFINITE,
+                         ids=[f"{n}-W{w}-S{s}" for n, w, s in WINDOW_NONFINITE])
+def test_window_nonfinite_unattended_rows(orc, name, window, sinks):
+    """NaN / infinite K and V in the tokens a window leaves out, inside blocks (and
+    16-token chunks) that still hold attended tokens: every output equals the oracle's,
+    which never reads those tokens, in all three schedules."""
+    cfg = (SMALL["llama8b"].replace(num_seqs=70, ctx_kind="fixed", ctx_params=tuple(range(1, 71)))
+           if name == "ragged" else SMALL[name])
+    w, g = _prepared(cfg)
+    kc, vc, _, _ = oracle_step(orc, w)
+    bt = free_blocks_outside_window(w, window, sinks)
+    n = _poison_unattended(w, g, kc, vc, window, sinks, bt)
+    assert n > 0
+    ref = _oracle_window(orc, w, kc, vc, window, sinks, bt)
+    assert np.isfinite(ref).all()
+    tables = torch.from_numpy(bt).cuda()
+    for part in (0, -1, 2 * w.cfg.block_size):
+        print(f"non-finite window case {name} W={window} S={sinks} partition={part} ({n} rows)", flush=True)
+        out = out_to_f64(_decode_window(g, window, sinks, tables, part))
+        assert_close_to_oracle(out, ref, w.cfg.kv_dtype, f"{name} W={window} S={sinks} part={part}")
