@@ -13,8 +13,9 @@
  *   - Every array argument is a DEVICE pointer owned by the caller (allocated by
  *     any HIP allocator, e.g. PyTorch).  The library allocates and frees nothing;
  *     its only global state is a per-device cache of kernel-occupancy queries
- *     (filled on first use, safe under concurrent calls).  Concurrent calls on
- *     different streams are safe as long as they do not write the same memory.
+ *     (filled on first use, safe under concurrent calls) and the scratch array of
+ *     paged_attention_decode_noalloc (below).  Concurrent calls on different streams
+ *     are safe as long as they do not write the same memory.
  *   - Every call is asynchronous on `stream` (NULL = the null stream).  Buffers
  *     must stay alive until the caller synchronises.  Host-visible argument
  *     errors are returned before anything is launched; no call synchronises
@@ -57,7 +58,9 @@ typedef enum {
   PKV_ERR_WORKSPACE = -5,   /* workspace too small, or bad partition size */
   PKV_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
   PKV_ERR_POOL_EXHAUSTED = -7, /* block pool: fewer free blocks than asked for */
-  PKV_ERR_BLOCK_STATE = -8  /* block pool: a block ID out of range, or not allocated */
+  PKV_ERR_BLOCK_STATE = -8, /* block pool: a block ID out of range, or not allocated */
+  PKV_ERR_SCRATCH = -9      /* paged_attention_decode_noalloc: the call needs more scratch
+                               than PKV_NOALLOC_SCRATCH_BYTES */
 } pkv_status;
 
 /* Every non-empty decode workspace starts with this many bytes of arrival counters,
@@ -206,6 +209,31 @@ int paged_attention_decode(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
                            int32_t max_context_len, float scale, void* out,
                            pkv_dtype out_dtype, int32_t partition_size, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Computes exactly what paged_attention_decode computes with the same
+ * arguments (the same schedules and kernels); the scratch those kernels need (arrival
+ * counters and partial results) lives in a file-scope device array of
+ * PKV_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds from this call's
+ * first use on it until the process ends.  The call allocates nothing.
+ *   Arguments: as paged_attention_decode, without workspace / workspace_bytes.
+ *   Errors: as paged_attention_decode; PKV_ERR_SCRATCH when the schedule needs more
+ *   than PKV_NOALLOC_SCRATCH_BYTES (paged_attention_workspace_size() tells how much:
+ *   e.g. more sequences or partitions than fit; use paged_attention_decode then).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ *   different streams without synchronisation, or from several host threads) race and
+ *   give undefined results.  Calls in order on one stream are safe: each call leaves
+ *   the array's counters zero, and its first use on a GPU clears them on `stream`.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int paged_attention_decode_noalloc(const void* q, pkv_dtype q_dtype, int32_t num_seqs,
+                                   int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                   const pkv_cache_desc* cache, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, float scale, void* out,
+                                   pkv_dtype out_dtype, int32_t partition_size, hipStream_t stream);
 
 /*
  * Decode attention over a sliding window with attention sinks: each query head attends

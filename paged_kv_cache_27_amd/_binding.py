@@ -21,10 +21,11 @@ _NAME_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "fp8": FP8_E4M3}
 
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_DTYPE", -3: "PKV_ERR_SHAPE",
           -4: "PKV_ERR_HEADS", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH",
-          -7: "PKV_ERR_POOL_EXHAUSTED", -8: "PKV_ERR_BLOCK_STATE"}
+          -7: "PKV_ERR_POOL_EXHAUSTED", -8: "PKV_ERR_BLOCK_STATE", -9: "PKV_ERR_SCRATCH"}
 
 EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_kv_write_positions", "paged_attention_schedule",
-            "paged_attention_workspace_size", "paged_attention_decode", "paged_attention_decode_window",
+            "paged_attention_workspace_size", "paged_attention_decode", "paged_attention_decode_noalloc",
+            "paged_attention_decode_window",
             "paged_attention_shared_prefix_workspace_size", "paged_attention_decode_shared_prefix",
             "paged_attention_prefill", "paged_kv_copy_blocks", "paged_kv_swap_out", "paged_kv_swap_in",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_alloc", "pkv_pool_share", "pkv_pool_release",
@@ -81,6 +82,10 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.POINTER(CacheDesc), vp, i32, vp, i32, f32, vp,
                                            ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp,
+                                                   ctypes.POINTER(CacheDesc), vp, i32, vp, i32, f32, vp,
+                                                   ctypes.c_int, i32, vp]
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
     lib.paged_attention_decode_window.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp,
                                                   ctypes.POINTER(CacheDesc), vp, i32, vp, i32, i32, i32,
                                                   f32, vp, ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
@@ -185,6 +190,8 @@ def pkv_status_string(status: int) -> str:
 
 # Size of the zero-filled counter header at the start of every decode workspace.
 WORKSPACE_HEADER_BYTES = 32768
+# Scratch held per GPU by paged_attention_decode_noalloc (PKV_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def pkv_abi_version() -> int:
@@ -403,6 +410,29 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
                int(partition_size), _ptr(workspace) if workspace is not None else None,
                workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   scale: float, out: torch.Tensor, max_context_len: int,
+                                   partition_size: int = 0, kv_dtype=None, k_scale: float = 1.0,
+                                   v_scale: float = 1.0, q_dtype=None, out_dtype=None,
+                                   shared_blocks: bool = False, stream=None) -> torch.Tensor:
+    """Decode attention into `out` as paged_attention_decode, with no workspace: the
+    library's per-GPU scratch array serves instead (see include/pagedkv.h; calls that
+    overlap on one GPU race)."""
+    lib = load_library()
+    desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale, shared_blocks)
+    n, hq, d = q.shape
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    _check("paged_attention_decode_noalloc",
+           lib.paged_attention_decode_noalloc(
+               _ptr(q), dtype_code(q_dtype if q_dtype is not None else q.dtype), n, hq,
+               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
+               block_tables.shape[1], _ptr(context_lens), int(max_context_len), float(scale),
+               _ptr(out), dtype_code(out_dtype if out_dtype is not None else out.dtype),
+               int(partition_size), _stream(stream)))
     return out
 
 

@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pkv_launch.h"
 
 namespace {
@@ -312,11 +315,55 @@ int run_decode(const Plan& plan, const void* q, int q_dtype, int32_t num_seqs, i
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
+// ---- scratch of the no-alloc decode ------------------------------------------------
+// One array per GPU, held from the library's first use on that GPU until the process
+// ends.  Host code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): the device address comes from hipGetSymbolAddress,
+// once per device with that device current, and is kept per device.
+__device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address; on its first use the counter header is cleared
+// on `stream` (a fill kernel), and every decode leaves it zero after that.
+int scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return PKV_ERR_LAUNCH;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) {
+    *out = ptr;
+    return PKV_OK;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return PKV_ERR_LAUNCH;
+    }
+    constexpr int kWords = (int)(pkv::kWsHeaderBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(zero_words_kernel, dim3(kWords / 256), dim3(256), 0, stream, (uint32_t*)ptr, kWords);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 7; }
+int32_t pkv_abi_version(void) { return 8; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -329,6 +376,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_LAUNCH: return "HIP launch error";
     case PKV_ERR_POOL_EXHAUSTED: return "block pool: not enough free blocks";
     case PKV_ERR_BLOCK_STATE: return "block pool: block ID out of range or not allocated";
+    case PKV_ERR_SCRATCH: return "the call needs more scratch than the no-alloc decode holds";
     default: return "unknown status";
   }
 }
@@ -481,6 +529,28 @@ int paged_attention_decode_window(const void* q, pkv_dtype q_dtype, int32_t num_
                     max_blocks_per_seq, context_lens, max_context_len, window, sinks, scale, out, out_dtype,
                     workspace, stream);
 }
+
+int paged_attention_decode_noalloc(const void* q, pkv_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                   const void* k_cache, const void* v_cache, const pkv_cache_desc* cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t max_context_len, float scale,
+                                   void* out, pkv_dtype out_dtype, int32_t partition_size, hipStream_t stream) {
+  int st = check_decode_call(q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                             max_blocks_per_seq, context_lens, max_context_len, 0, 0, out, out_dtype);
+  if (st || num_seqs == 0) return st;
+  Plan plan;
+  st = plan_decode(cache, q_dtype, num_seqs, num_q_heads, max_context_len, partition_size, &plan);
+  if (st) return st;
+  if (plan.ws_bytes > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (plan.ws_bytes) {
+    st = scratch_for_current_device(stream, &ws);
+    if (st) return st;
+  }
+  return run_decode(plan, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables,
+                    max_blocks_per_seq, context_lens, max_context_len, 0, 0, scale, out, out_dtype, ws, stream);
+}
+
 
 size_t paged_attention_shared_prefix_workspace_size(const pkv_cache_desc* cache, pkv_dtype q_dtype,
                                                     int32_t num_seqs, int32_t num_q_heads,

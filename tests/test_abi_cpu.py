@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pkv.pkv_abi_version() == 7
+    assert pkv.pkv_abi_version() == 8
 
 
 def test_cache_desc_mirror_matches_the_c_layout(tmp_path):
@@ -52,10 +52,12 @@ def test_cache_desc_mirror_matches_the_c_layout(tmp_path):
 def test_workspace_header_constant_matches_header():
     m = re.search(r"#define\s+PKV_WORKSPACE_HEADER_BYTES\s+(\d+)", HEADER.read_text())
     assert m and int(m.group(1)) == pkv.WORKSPACE_HEADER_BYTES
+    m = re.search(r"#define\s+PKV_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", HEADER.read_text())
+    assert m and int(m.group(1)) << int(m.group(2)) == pkv.NOALLOC_SCRATCH_BYTES
 
 
 def test_status_strings():
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert pkv.pkv_status_string(code) != "unknown status"
     assert pkv.pkv_status_string(-99) == "unknown status"
 
@@ -71,6 +73,24 @@ def _decode(lib, desc, q_dtype=pkv.BF16, n=2, hq=4, out_dtype=pkv.BF16, maxb=4, 
             part=0, ws=None, wsb=0, q=FAKE, bt=FAKE):
     return lib.paged_attention_decode(q, q_dtype, n, hq, FAKE, FAKE, ctypes.byref(desc), bt, maxb,
                                       FAKE, maxctx, 0.1, FAKE, out_dtype, part, ws, wsb, None)
+
+
+def test_noalloc_decode_argument_errors():
+    """The no-alloc decode checks its arguments as the decode does, and refuses a call
+    whose schedule needs more than its fixed scratch before touching the device."""
+    lib = pkv.load_library()
+    call = lambda desc, n=2, hq=4, maxb=4, maxctx=40, part=0, q=FAKE: lib.paged_attention_decode_noalloc(
+        q, pkv.BF16, n, hq, FAKE, FAKE, ctypes.byref(desc), FAKE, maxb, FAKE, maxctx, 0.1, FAKE, pkv.BF16, part,
+        None)
+    assert call(_desc(head_dim=96)) == -3
+    assert call(_desc(), hq=5) == -4
+    assert call(_desc(), q=None) == -1
+    assert call(_desc(), part=24) == -5          # not a multiple of the block size
+    assert call(_desc(), n=0) == 0                 # nothing to do
+    # 4000 sequences x 32 heads x 256 partitions of partials: far beyond the scratch
+    need = pkv.paged_attention_workspace_size(_desc(num_kv_heads=8), pkv.BF16, 4000, 32, 4096, 16)
+    assert need > pkv.NOALLOC_SCRATCH_BYTES
+    assert call(_desc(num_kv_heads=8), n=4000, hq=32, maxb=256, maxctx=4096, part=16) == -9
 
 
 def test_decode_argument_errors():
