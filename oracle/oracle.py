@@ -23,20 +23,36 @@ _i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 
 
-def build(out: Path | str = DEFAULT_LIB, mutation: int = 0) -> Path:
-    """Compile oracle.c with gcc (IEEE fp64, no contraction, OpenMP)."""
-    out = Path(out)
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-fno-fast-math", f"-DORACLE_MUTATION={int(mutation)}", str(SOURCE), "-o",
-           str(out) + ".tmp", "-lm"]
+SANITIZED_LIB = HERE / "liboracle_asan.so"
+# The sanitizer build uses ROCm's clang, so that it shares one AddressSanitizer runtime with
+# the library's sanitizer build (paged_kv_cache_27_amd/build.py); OpenMP from its libomp.
+CLANG = "/opt/rocm/llvm/bin/clang"
+
+
+def build(out: Path | str = DEFAULT_LIB, mutation: int = 0, sanitize: bool = False) -> Path:
+    """Compile oracle.c with gcc (IEEE fp64, no contraction, OpenMP).  sanitize: with clang
+    under AddressSanitizer and UndefinedBehaviorSanitizer instead (default output
+    liboracle_asan.so), for the CPU test suite run against it."""
+    if sanitize:
+        out = Path(out) if Path(out) != DEFAULT_LIB else SANITIZED_LIB
+        cmd = [CLANG, "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer", f"-DORACLE_MUTATION={int(mutation)}", str(SOURCE), "-o",
+               str(out) + ".tmp", "-lm"]
+    else:
+        out = Path(out)
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", f"-DORACLE_MUTATION={int(mutation)}", str(SOURCE), "-o",
+               str(out) + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(str(out) + ".tmp", out)
     return out
 
 
 class Oracle:
-    def __init__(self, path: Path | str = DEFAULT_LIB):
-        path = Path(path)
+    def __init__(self, path: Path | str | None = None):
+        # PKV_ORACLE_LIB selects another build (the sanitizer build, for instance)
+        path = Path(path if path is not None else os.environ.get("PKV_ORACLE_LIB", DEFAULT_LIB))
         if not path.exists():
             build(path)
         self.lib = lib = ctypes.CDLL(str(path))

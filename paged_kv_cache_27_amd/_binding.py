@@ -54,12 +54,14 @@ class PagedKVError(RuntimeError):
 _lib = None
 
 
-def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
-    """Load (once) the HIP library; raise if it has not been built."""
+def load_library(path: Path | str | None = None) -> ctypes.CDLL:
+    """Load (once) the HIP library; raise if it has not been built.  PKV_LIBRARY selects
+    another build of it (the sanitizer build of the host code, for instance)."""
     global _lib
     if _lib is not None:
         return _lib
-    path = Path(path)
+    import os
+    path = Path(path if path is not None else os.environ.get("PKV_LIBRARY", LIB_PATH))
     if not path.exists():
         raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_27_amd.build`")
     lib = ctypes.CDLL(str(path))

@@ -45,6 +45,44 @@ def _compile(src: Path) -> Path:
     return obj
 
 
+ASAN_LIB = BUILD / "asan" / "libpagedkv_asan.so"
+# Host code only: each sanitizer flag applies to the host compilation (-Xarch_host); the
+# device code is the regular build's.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-g"]
+
+
+def build_sanitized(verbose: bool = True) -> Path:
+    """The library with its host-only sources (api.cpp: argument checks, planning, the
+    pool's front end; pool.cpp: the block pool) compiled under AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the kernels' objects of the regular build
+    (built first if missing), into _build/asan/libpagedkv_asan.so.  The CPU test suite
+    runs against it with the sanitizer runtime preloaded (tests/test_sanitizers_cpu.py)."""
+    out_dir = ASAN_LIB.parent
+    out_dir.mkdir(parents=True, exist_ok=True)
+    kernels = sorted(CSRC.glob("*.hip"))
+    if not all((BUILD / (k.name + ".o")).exists() for k in kernels):
+        build(verbose=False)
+    objs = [BUILD / (k.name + ".o") for k in kernels]
+    for src in sorted(CSRC.glob("*.cpp")):
+        obj = out_dir / (src.name + ".o")
+        cmd = [HIPCC, *FLAGS, *SANITIZE_FLAGS, "-x", "hip", "-c", str(src), "-o", str(obj)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {src.name} (sanitizer build)")
+        objs.append(obj)
+    tmp = ASAN_LIB.with_suffix(".so.tmp")
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                    "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *map(str, objs), "-o", str(tmp)],
+                   check=True)
+    os.replace(tmp, ASAN_LIB)
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 def build(verbose: bool = True) -> Path:
     BUILD.mkdir(exist_ok=True)
     sources = sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))

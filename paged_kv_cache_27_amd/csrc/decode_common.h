@@ -776,7 +776,7 @@ __device__ __forceinline__ void run_chunks(W& wd, int c_begin, int c_end, int st
 // once per batch.  part(p) returns the partial's (m, l, acc-row) pointers.  vnorm
 // scales the result (the fp8 V scale).  Writes out[row + d].
 constexpr int kMergeThreads = 256;
-constexpr int kMergeBatch = 8;
+constexpr int kMergeBatch = 32;  // 64 partitions of 128 dims: one batch per thread
 __device__ __forceinline__ void lse_add(float& M, float& L, float& A, float m, float l, float x) {
   const float Mn = fmaxf(M, m);
   const float base = Mn == kNegInf ? 0.0f : Mn;

@@ -57,11 +57,38 @@ template <int KV, int GP> struct SkShape {
   static constexpr int NW = KV == kF32 ? 4 : (GP <= 8 ? 8 : 4);
 };
 
+// Quotient of non-negative operands: a 32-bit division (a few instructions) when both
+// fit in 31 bits, as they do for any realistic unit count, else the 64-bit one.
+__device__ __forceinline__ long long udiv(long long a, long long b) {
+  if (((a | b) >> 31) == 0) return (long long)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
 // floor-division split of T items into P parts: part p holds [T p / P, T (p+1) / P);
 // owner(x) is the part holding item x (T >= P >= 1, so no part is empty).
-__device__ __forceinline__ long long split_begin(long long T, long long P, long long p) { return T * p / P; }
+__device__ __forceinline__ long long split_begin(long long T, long long P, long long p) { return udiv(T * p, P); }
 __device__ __forceinline__ long long split_owner(long long T, long long P, long long x) {
-  return ((x + 1) * P - 1) / T;
+  return udiv((x + 1) * P - 1, T);
+}
+
+// The largest s in [0, N) with cum[s] <= r, for non-decreasing cum (N + 1 entries) with
+// cum[0] = 0 <= r < cum[N]: the sequence holding chunk r (an empty context, whose cum
+// equals the next one's, is skipped).  Each round the wave samples 64 evenly spaced
+// entries of the remaining span and counts those <= r with a ballot -- they form a
+// prefix -- narrowing the span 64-fold (one round up to 64 sequences, two up to 4096).
+__device__ __forceinline__ int find_seq(const int* cum, int N, int r) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, span = N;
+  while (span > 1) {
+    const int step = (span + 63) >> 6;
+    const int idx = lo + lane * step;
+    const bool le = idx < lo + span && cum[idx] <= r;
+    const int c = __popcll(__ballot(le));  // >= 1: lane 0 reads cum[lo] <= r
+    const int end = lo + span;
+    lo += (c - 1) * step;
+    span = min(step, end - lo);
+  }
+  return lo;
 }
 
 // Per-lane view of the G x D output rows of one segment: lane t handles float4 t,
@@ -153,8 +180,17 @@ decode_sk_kernel(const DecodeArgs a) {
     if constexpr (PRE) return max(0, ((a.context_lens[i] + 15) >> 4) - (a.seq_begin[i] >> 4));
     return attended_chunk_count(a.context_lens[i], a.window, a.sinks);
   };
+  // a thread's first few counts are kept in registers (their loads issued together) for
+  // the second pass below; beyond that (thousands of sequences) they are read again
+  constexpr int kKeep = 4;
+  int kept[kKeep];
   int local = 0;
-  for (int i = i0s; i < i1s; ++i) local += chunks_of(i);
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    kept[k] = i0s + k < i1s ? chunks_of(i0s + k) : 0;
+    local += kept[k];
+  }
+  for (int i = i0s + kKeep; i < i1s; ++i) local += chunks_of(i);
   int incl = local;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -166,7 +202,12 @@ decode_sk_kernel(const DecodeArgs a) {
   __syncthreads();
   int run_sum = incl - local;
   for (int w2 = 0; w2 < wv; ++w2) run_sum += wave_tot[w2];
-  for (int i = i0s; i < i1s; ++i) {
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    if (i0s + k < i1s) sk_cum[i0s + k] = run_sum;
+    run_sum += kept[k];
+  }
+  for (int i = i0s + kKeep; i < i1s; ++i) {
     sk_cum[i] = run_sum;
     run_sum += chunks_of(i);
   }
@@ -245,16 +286,11 @@ decode_sk_kernel(const DecodeArgs a) {
 
   auto seg_of = [&](long long u) {
     Seg x;
-    x.g = (int)(u / C);
+    x.g = (int)udiv(u, C);
     const int r = (int)(u - (long long)x.g * C);
-    int lo = 0, hi = N;  // largest s with sk_cum[s] <= r (skips empty contexts)
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sk_cum[mid] <= r) lo = mid; else hi = mid;
-    }
     // Values read from LDS are wave-uniform; say so, so that what derives from them
     // (block-table addresses in particular) stays on the scalar path.
-    x.s = __builtin_amdgcn_readfirstlane(lo);
+    x.s = __builtin_amdgcn_readfirstlane(find_seq(sk_cum, N, r));
     const int cs = __builtin_amdgcn_readfirstlane(sk_cum[x.s]);
     x.n = __builtin_amdgcn_readfirstlane(sk_cum[x.s + 1]) - cs;
     x.xs = (long long)x.g * C + cs;

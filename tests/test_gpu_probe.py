@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import paged_kv_cache_27_amd as pkv
+from paged_kv_cache_27_amd._binding import LIB_PATH
 
 pytestmark = pytest.mark.gpu
 
@@ -15,7 +16,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("tile_bytes", [1024, 2048, 4096, 8192])
 def test_probe_reads_tiles(tile_bytes):
     assert torch.cuda.is_available(), "GPU tests need a GPU"
-    lib = ctypes.CDLL(str(Path(pkv.load_library()._name).with_name("libpkv_probe.so")))
+    lib = ctypes.CDLL(str(LIB_PATH.with_name("libpkv_probe.so")))  # built beside the package library
     f = lib.pkv_probe_read_tiles
     f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p]
