@@ -390,26 +390,25 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return bits_f32(r[0]) + bits_f32(r[1]);
 }
 
-// P.V operand handling per cache dtype.  A fragment: 4 elements, element (lane & 3)
-// holds the probability, the others zero.
+// P.V operand handling per cache dtype.  A fragment: 4 16-bit elements (two words),
+// element (lane & 3) holds the probability, the others zero.  The element is placed by
+// two byte permutes whose selectors (s0, s1: one per word, fixed per lane) take the
+// 16-bit value from bytes kSrc of a 32-bit source and zero the rest.
 template <int KV> struct Pv;
 template <> struct Pv<kBF16> {
   static constexpr bool kSplit = true;
+  static constexpr uint32_t kSrc = 0x0302u;  // the upper half of fp32 bits
   using frag = bf16x4_t;
   // V: two 32-bit words = 4 bf16
   __device__ __forceinline__ static frag vfrag(const uint32_t* w, int half) {
     return __builtin_bit_cast(frag, make_uint2(w[2 * half], w[2 * half + 1]));
   }
   // p = hi + lo, hi the upper half of p's fp32 bits, lo the bf16 truncation of the rest.
-  __device__ __forceinline__ static void pfrag(float p, int lane, frag& hi, frag& lo) {
+  __device__ __forceinline__ static void pfrag(float p, uint32_t s0, uint32_t s1, frag& hi, frag& lo) {
     const uint32_t pb = f32_bits(p);
-    const uint32_t hb = pb >> 16;
-    const uint32_t lb = f32_bits(p - bits_f32(pb & 0xffff0000u)) >> 16;
-    const uint32_t sh = (lane & 1) * 16;
-    const bool low = (lane & 2) == 0;
-    const uint32_t wh = hb << sh, wl = lb << sh;
-    hi = __builtin_bit_cast(frag, make_uint2(low ? wh : 0u, low ? 0u : wh));
-    lo = __builtin_bit_cast(frag, make_uint2(low ? wl : 0u, low ? 0u : wl));
+    const uint32_t rb = f32_bits(p - bits_f32(pb & 0xffff0000u));
+    hi = __builtin_bit_cast(frag, make_uint2(__builtin_amdgcn_perm(0u, pb, s0), __builtin_amdgcn_perm(0u, pb, s1)));
+    lo = __builtin_bit_cast(frag, make_uint2(__builtin_amdgcn_perm(0u, rb, s0), __builtin_amdgcn_perm(0u, rb, s1)));
   }
   __device__ __forceinline__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -417,19 +416,17 @@ template <> struct Pv<kBF16> {
 };
 template <> struct Pv<kF16> {
   static constexpr bool kSplit = true;
+  static constexpr uint32_t kSrc = 0x0100u;  // an f16 value in the low half
   using frag = f16x4_t;
   __device__ __forceinline__ static frag vfrag(const uint32_t* w, int half) {
     return __builtin_bit_cast(frag, make_uint2(w[2 * half], w[2 * half + 1]));
   }
-  __device__ __forceinline__ static void pfrag(float p, int lane, frag& hi, frag& lo) {
+  __device__ __forceinline__ static void pfrag(float p, uint32_t s0, uint32_t s1, frag& hi, frag& lo) {
     const _Float16 h = (_Float16)p;
     const _Float16 r = (_Float16)(p - (float)h);
-    const uint32_t sh = (lane & 1) * 16;
-    const bool low = (lane & 2) == 0;
-    const uint32_t wh = (uint32_t)__builtin_bit_cast(uint16_t, h) << sh;
-    const uint32_t wl = (uint32_t)__builtin_bit_cast(uint16_t, r) << sh;
-    hi = __builtin_bit_cast(frag, make_uint2(low ? wh : 0u, low ? 0u : wh));
-    lo = __builtin_bit_cast(frag, make_uint2(low ? wl : 0u, low ? 0u : wl));
+    const uint32_t hb = __builtin_bit_cast(uint16_t, h), rb = __builtin_bit_cast(uint16_t, r);
+    hi = __builtin_bit_cast(frag, make_uint2(__builtin_amdgcn_perm(0u, hb, s0), __builtin_amdgcn_perm(0u, hb, s1)));
+    lo = __builtin_bit_cast(frag, make_uint2(__builtin_amdgcn_perm(0u, rb, s0), __builtin_amdgcn_perm(0u, rb, s1)));
   }
   __device__ __forceinline__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -437,6 +434,7 @@ template <> struct Pv<kF16> {
 };
 template <> struct Pv<kFP8> {
   static constexpr bool kSplit = false;
+  static constexpr uint32_t kSrc = 0x0100u;
   using frag = f16x4_t;
   // V: one 32-bit word = 4 e4m3fn codes, converted exactly to f16.
   __device__ __forceinline__ static frag vfrag(const uint32_t* w, int half) {
@@ -445,16 +443,16 @@ template <> struct Pv<kFP8> {
     frag r = {a[0], a[1], b[0], b[1]};
     return r;
   }
-  __device__ __forceinline__ static void pfrag(float p, int lane, frag& hi, frag&) {
-    const uint32_t sh = (lane & 1) * 16;
-    const bool low = (lane & 2) == 0;
-    const uint32_t wh = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p) << sh;
-    hi = __builtin_bit_cast(frag, make_uint2(low ? wh : 0u, low ? 0u : wh));
+  __device__ __forceinline__ static void pfrag(float p, uint32_t s0, uint32_t s1, frag& hi, frag&) {
+    const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)p);
+    hi = __builtin_bit_cast(frag, make_uint2(__builtin_amdgcn_perm(0u, hb, s0), __builtin_amdgcn_perm(0u, hb, s1)));
   }
   __device__ __forceinline__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
 };
+
+constexpr float kDecodeSlack = 8.0f;  // log2 units: decode weights stay <= 2^8 between rescales
 
 template <int KV, int D> struct MfmaChunk {
   static constexpr int EB = DtInfo<KV>::bytes;
@@ -486,7 +484,14 @@ struct MfmaDecoder {
   typename T::frag qf[HS][NC * T::SUB];
   float m[HS], l[HS], lfin[HS];
   f32x4_t acc[HS][HALVES];
-  float scale_l2;
+  // Scores are taken raw (S = K Q^T) and scaled inside the exponent, 2^(c s - m) with
+  // c = |scale| log2(e) (x |k_scale| for fp8) > 0, so that the maximum can be taken on
+  // raw scores: a negative scale flips the sign of Q instead (exact), a zero one zeroes
+  // Q (all scores 0: uniform weights).
+  float c_l2;
+  uint32_t qflip;
+  bool qzero;
+  uint32_t psel0, psel1;  // P fragment placement (Pv::pfrag)
   const uint8_t* kc;
   const uint8_t* vc;
   const int32_t* bt;
@@ -495,8 +500,15 @@ struct MfmaDecoder {
 
   __device__ __forceinline__ void init(const DecodeArgs& a, float*, float*) {
     lane = threadIdx.x & 63;
-    scale_l2 = a.scale * kLog2e;
-    if constexpr (KV == kFP8) scale_l2 *= a.k_scale;
+    float ks = 1.0f;
+    if constexpr (KV == kFP8) ks = a.k_scale;
+    qflip = (a.scale < 0.0f) != (ks < 0.0f) ? 0x80008000u : 0u;
+    qzero = a.scale == 0.0f || ks == 0.0f;
+    c_l2 = (a.scale != 0.0f ? __builtin_fabsf(a.scale) : 1.0f) * kLog2e * (ks != 0.0f ? __builtin_fabsf(ks) : 1.0f);
+    // element lane & 3 of the P fragment: word (lane & 3) / 2, half (lane & 1)
+    const uint32_t pat = (lane & 1) ? ((P::kSrc << 16) | 0x0c0cu) : (0x0c0c0000u | P::kSrc);
+    psel0 = (lane & 2) ? 0x0c0c0c0cu : pat;
+    psel1 = (lane & 2) ? pat : 0x0c0c0c0cu;
     kc = (const uint8_t*)a.k_cache;
     vc = (const uint8_t*)a.v_cache;
     BS = a.block_size;
@@ -521,8 +533,14 @@ struct MfmaDecoder {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int j = 0; j < T::SUB; ++j)
-          qf[hs][c * T::SUB + j] = qvalid ? T::qload(qrow, T::qdim(c, grp, j)) : T::zero();
+        for (int j = 0; j < T::SUB; ++j) {
+          typename T::frag f = T::zero();
+          if (qvalid && !qzero) {
+            const uint4 w = __builtin_bit_cast(uint4, T::qload(qrow, T::qdim(c, grp, j)));
+            f = __builtin_bit_cast(typename T::frag, make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip));
+          }
+          qf[hs][c * T::SUB + j] = f;
+        }
       m[hs] = kNegInf;
       l[hs] = 0.0f;
 #pragma unroll
@@ -588,26 +606,30 @@ struct MfmaDecoder {
         for (int hs = 0; hs < HS; ++hs) S[hs] = T::mma(kf, qf[hs][c2 * T::SUB + j], S[hs]);
       }
     const int tb = ct + (lane >> 4);
-    // ---- online softmax, one head per lane (duplicated over lane & 3)
+    // ---- online softmax, one head per lane (duplicated over lane & 3).  Lazy
+    // rescaling: the reference max m moves only when a score exceeds it by more than
+    // kDecodeSlack (or on the first attended token), so weights 2^(c s - m) stay <= 2^8
+    // and the rescale of l and acc is rare; (m, l, acc) stay one consistent partial.
     float p[HS][4], alpha[HS];
-    bool changed = false;
+    bool moved = false;
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
       float s[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s[k] = keep(tb + 4 * k) ? S[hs][k] * scale_l2 : kNegInf;
+      for (int k = 0; k < 4; ++k) s[k] = keep(tb + 4 * k) ? S[hs][k] : kNegInf;
       float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      bm = xor32_max(xor16_max(bm));
-      const float mn = fmaxf(m[hs], bm);
-      changed |= mn > m[hs];
+      bm = xor32_max(xor16_max(bm)) * c_l2;
+      const bool mv = bm > m[hs] + kDecodeSlack;
+      moved |= mv;
+      const float mn = mv ? bm : m[hs];
       const float base = mn == kNegInf ? 0.0f : mn;
-      alpha[hs] = fast_exp2(m[hs] - base);
+      alpha[hs] = fast_exp2(m[hs] - base);  // 1 unless m moved (0 from -inf)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) p[hs][k] = fast_exp2(s[k] - base);
+      for (int k = 0; k < 4; ++k) p[hs][k] = fast_exp2(__builtin_fmaf(s[k], c_l2, -base));
       l[hs] = l[hs] * alpha[hs] + ((p[hs][0] + p[hs][1]) + (p[hs][2] + p[hs][3]));
       m[hs] = mn;
     }
-    if (__ballot(changed) != 0) {
+    if (__ballot(moved) != 0) {
       // the accumulator of lane l belongs to head 4hs + l/16, whose factor lane 4(l/16) holds
 #pragma unroll
       for (int hs = 0; hs < HS; ++hs) {
@@ -639,7 +661,7 @@ struct MfmaDecoder {
 #pragma unroll
       for (int hs = 0; hs < HS; ++hs) {
         typename P::frag ahi, alo;
-        P::pfrag(p[hs][k], lane, ahi, alo);
+        P::pfrag(p[hs][k], psel0, psel1, ahi, alo);
 #pragma unroll
         for (int hf = 0; hf < HALVES; ++hf) {
           acc[hs][hf] = P::mma(ahi, vf[hf], acc[hs][hf]);
