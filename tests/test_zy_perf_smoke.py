@@ -1,0 +1,47 @@
+"""Performance smoke (GPU only): every decode workload's decode call, timed as bench.py
+times it (layered over four cold per-layer cache copies), against the last recorded run
+in tests/golden/perf_baseline.json (written from a `bench.py --all --json-out` result by
+tests/golden/perf_baseline.py).  It fails on a slowdown beyond run-to-run noise: more
+than 20 % plus 3 us (the 3 us cover launch jitter on the microsecond-scale tiny
+workload).  Collected after the parity tests, so that a failure here hides none of them.
+"""
+import json
+from pathlib import Path
+
+import pytest
+import torch
+
+import bench
+import paged_kv_cache_27_amd as pkv
+from workloads import CONFIGS, EXTRA_CONFIGS, make_workload
+
+pytestmark = pytest.mark.gpu
+
+BASELINE = json.loads((Path(__file__).parent / "golden" / "perf_baseline.json").read_text())
+REL, ABS_US = 0.20, 3.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.load_library()
+
+
+@pytest.mark.parametrize("name", sorted(BASELINE["decode_us_layered"]))
+def test_decode_no_regression(name):
+    cfg = next(c for c in CONFIGS + EXTRA_CONFIGS if c.name == name)
+    w = make_workload(cfg)
+    st = bench.Step(w)
+    copies = [(st.k_cache, st.v_cache)] + [(st.k_cache.clone(), st.v_cache.clone()) for _ in range(3)]
+
+    def run(k, v):
+        st.k_cache, st.v_cache = k, v
+        st.decode()
+
+    us = min(bench.layered_ms(run, copies, 10) * 1e3 for _ in range(3))
+    ref = BASELINE["decode_us_layered"][name]
+    limit = ref * (1.0 + REL) + ABS_US
+    print(f"perf smoke {name}: {us:.1f} us (last recorded {ref:.1f} us, limit {limit:.1f} us)", flush=True)
+    del st, copies
+    torch.cuda.empty_cache()
+    assert us <= limit, f"{name}: decode {us:.1f} us against {ref:.1f} us recorded (limit {limit:.1f})"
