@@ -586,8 +586,8 @@ def cpu_model():
     return None
 
 
-# Oracle threads: the host CPUs this process may run on, at most the 16 a one-GPU machine's
-# share holds (its affinity mask can list more CPUs than the share).
+# Oracle threads: the host CPUs this process may run on, at most 16, the CPU share one GPU
+# of a shared MI355X host gets (its affinity mask can list more CPUs than the share).
 CPU_SHARE = 16
 
 
@@ -613,7 +613,7 @@ def cpu_baseline(w, budget_s):
     res["single_thread"] = {"value": one["value"], "unit": "GB/s", "cores": 1, "sample": one["sample"]}
     res["affinity_cpus"] = affinity
     res["cpu_model"] = cpu_model()
-    res["threads_note"] = f"threads = min(affinity {affinity}, the box's {CPU_SHARE}-CPU share)"
+    res["threads_note"] = f"threads = min(affinity {affinity}, the {CPU_SHARE}-CPU share of one GPU)"
     return res
 
 

@@ -17,7 +17,7 @@ from workloads import CONFIGS, EXTRA_CONFIGS, make_workload
 
 pytestmark = pytest.mark.gpu
 
-BASELINE = json.loads((Path(__file__).parent / "golden" / "perf_baseline.json").read_text())
+RECORDED = json.loads((Path(__file__).parent / "golden" / "perf_baseline.json").read_text())
 REL, ABS_US = 0.20, 3.0
 
 
@@ -27,7 +27,7 @@ def _gpu():
     pkv.load_library()
 
 
-@pytest.mark.parametrize("name", sorted(BASELINE["decode_us_layered"]))
+@pytest.mark.parametrize("name", sorted(RECORDED["decode_us_layered"]))
 def test_decode_no_regression(name):
     cfg = next(c for c in CONFIGS + EXTRA_CONFIGS if c.name == name)
     w = make_workload(cfg)
@@ -39,7 +39,7 @@ def test_decode_no_regression(name):
         st.decode()
 
     us = min(bench.layered_ms(run, copies, 10) * 1e3 for _ in range(3))
-    ref = BASELINE["decode_us_layered"][name]
+    ref = RECORDED["decode_us_layered"][name]
     limit = ref * (1.0 + REL) + ABS_US
     print(f"perf smoke {name}: {us:.1f} us (last recorded {ref:.1f} us, limit {limit:.1f} us)", flush=True)
     del st, copies
