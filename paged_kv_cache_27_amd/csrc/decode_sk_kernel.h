@@ -153,9 +153,12 @@ struct Seg {
 
 // PRE: each sequence's first seq_begin[s] tokens were attended by the shared-prefix
 // kernel, which left pre_splits partials per (sequence, query head) in pre_part; this
-// kernel streams only the rest of each context and folds those partials in wherever it
-// writes a final output.  A piece covering a whole segment then waits in a third LDS
-// slot of its wave for that fold instead of being written straight out.
+// kernel streams only the rest of each context and folds those partials in once per
+// segment: into the result of the segment's first piece, from LDS that the piece's wave
+// filled while it streamed (when the segment's partial rows fit in its LDS area), or
+// else, read from memory, wherever it writes a final output.  A piece covering a whole
+// segment waits in a third LDS slot of its wave for that fold instead of being written
+// straight out.
 template <int KV, int Q, int D, int GP, int NW, bool NT, bool PRE>
 __global__ void __launch_bounds__(64 * NW)
 decode_sk_kernel(const DecodeArgs a) {
@@ -172,6 +175,14 @@ decode_sk_kernel(const DecodeArgs a) {
   __shared__ float lds_alpha[NW][GP];
   __shared__ float lds_inv[NW][GP];
   __shared__ int wave_tot[NW];
+  // PRE: the prefix partials of a segment (its G heads x pre_splits slices, contiguous
+  // rows of 4 + D floats) are loaded straight into this wave's LDS area when the wave
+  // starts the segment's first piece, and folded into that piece's result when it ends,
+  // so no output waits on them.  Up to kPreRows rows, in whole 1 KiB wave loads.
+  constexpr bool PRE_LDS = PRE && GP <= 4;
+  constexpr int kPreRows = 16;
+  constexpr int PRE_FLOATS = (kPreRows * (4 + D) * 4 + 1023) / 1024 * 256;
+  __shared__ __attribute__((aligned(16))) float lds_pre[PRE_LDS ? NW : 1][PRE_LDS ? PRE_FLOATS : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int N = a.num_seqs;
@@ -257,6 +268,38 @@ decode_sk_kernel(const DecodeArgs a) {
     }
   };
 
+  // Prefix partials in LDS (PRE_LDS, when a segment's G x pre_splits rows fit): issued
+  // before the piece's first K/V loads, so they arrive with them.  Bytes past the
+  // segment's rows read as zeros (the resource ends there) into the rest of the area.
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const bool pre_early = PRE_LDS && G * a.pre_splits <= kPreRows;
+  auto prefetch_prefix = [&](int s, int g) {
+    if constexpr (PRE_LDS) {
+      const int T = a.pre_splits;
+      const float* base = a.pre_part + ((size_t)s * a.num_q_heads + (size_t)g * G) * T * PSTRIDE;
+      const __amdgpu_buffer_rsrc_t r = tile_rsrc((const uint8_t*)base, G * T * PSTRIDE * (int)sizeof(float));
+#pragma unroll
+      for (int i = 0; i < PRE_FLOATS / 256; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)&lds_pre[wvu][256 * i],
+                                                 16, 16 * lane + 1024 * i, 0, 0, 0);
+    }
+  };
+  // Fold the partials prefetched into this wave's LDS area into rs.
+  auto add_prefix_lds = [&](RS& rs) {
+    if constexpr (PRE_LDS) {
+      __builtin_amdgcn_s_waitcnt(0);  // the loads into LDS are complete
+      wave_lds_sync();
+      const int T = a.pre_splits;
+      for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int k = 0; k < RS::EPL; ++k) {
+          const float* pp = &lds_pre[wvu][(rs.hh[k] * T + t) * PSTRIDE];
+          rs.add(k, pp[0], pp[1], *(const float4*)(pp + 4 + rs.dd[k]));
+        }
+      }
+    }
+  };
+
   // Contexts with no chunk to stream own no unit: zeros, or (PRE) their prefix alone;
   // spread over all waves.
   {
@@ -314,6 +357,9 @@ decode_sk_kernel(const DecodeArgs a) {
   auto do_piece = [&](const Seg& X, long long u0, long long u1) {
     const int cb = (int)(u0 - X.xs), ce = (int)(u1 - X.xs);
     const int ctx = a.context_lens[X.s];
+    // PRE: the piece starting a segment with a shared prefix takes the prefix in
+    const bool fold_here = pre_early && cb == 0 && a.seq_begin[X.s] > 0;
+    if (fold_here) prefetch_prefix(X.s, X.g);
     wd.begin(a, X.s, X.g, ctx);
     if constexpr (PRE) {
       const int cb0 = a.seq_begin[X.s] >> 4;  // first streamed chunk of the context
@@ -359,6 +405,30 @@ decode_sk_kernel(const DecodeArgs a) {
     // The waves of this workgroup that cover X: i0 .. i1.
     const int i0 = (int)split_owner(Lb, NWn, max(X.xs, ub) - ub);
     const int i1 = (int)split_owner(Lb, NWn, min(X.xe, ue) - 1 - ub);
+    if (fold_here) {  // the segment's first piece: fold in the prefix from LDS
+      wave_lds_sync();
+      RS rs;
+      rs.init(lane, G);
+#pragma unroll
+      for (int k = 0; k < RS::EPL; ++k)
+        rs.add(k, lp[rs.hh[k]], lp[GP + rs.hh[k]], *(const float4*)(lp + L_::ACC + rs.hh[k] * D + rs.dd[k]));
+      add_prefix_lds(rs);
+      if (full) {  // the whole segment: write
+        rs.write_out(a, row0, vnorm);
+        wave_lds_sync();  // the slot is reused by this wave's next whole segment
+        return;
+      }
+      // else the piece's partial, now with the prefix, goes back to its slot
+#pragma unroll
+      for (int k = 0; k < RS::EPL; ++k) {
+        if (!rs.ok[k]) continue;
+        *(float4*)(lp + L_::ACC + rs.hh[k] * D + rs.dd[k]) = rs.A[k];
+        if (rs.dd[k] == 0) {
+          lp[rs.hh[k]] = rs.M[k];
+          lp[GP + rs.hh[k]] = rs.L[k];
+        }
+      }
+    }
     if (PRE && full) {  // this wave holds the whole segment: fold in the prefix, write
       wave_lds_sync();
       RS rs;
@@ -395,7 +465,7 @@ decode_sk_kernel(const DecodeArgs a) {
         rs.add(k, q[rs.hh[k]], q[GP + rs.hh[k]], *(const float4*)(q + L_::ACC + rs.hh[k] * D + rs.dd[k]));
     }
     if (X.xs >= ub && X.xe <= ue) {  // X lies inside this workgroup's range
-      add_prefix(rs, X.s, X.g);
+      if (!pre_early) add_prefix(rs, X.s, X.g);
       rs.write_out(a, row0, vnorm);
       return;
     }
@@ -438,7 +508,7 @@ decode_sk_kernel(const DecodeArgs a) {
         fin.add(k, m, l, make_float4(bits_f32(x.x), bits_f32(x.y), bits_f32(x.z), bits_f32(x.w)));
       }
     }
-    add_prefix(fin, X.s, X.g);
+    if (!pre_early) add_prefix(fin, X.s, X.g);
     fin.write_out(a, row0, vnorm);
     if (lane == 0) __hip_atomic_store(a.sk_count + b0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
