@@ -73,6 +73,12 @@ CASES = {
     "fp8-bf16q": PREFIX.replace(num_seqs=11, prefix_groups=3, kv_dtype="fp8", ctx_params=(96, 0, 90)),
     "fp8-f16q-d64-g8": PREFIX.replace(num_seqs=7, head_dim=64, num_q_heads=8, num_kv_heads=1, q_dtype="f16",
                                       kv_dtype="fp8", out_dtype="f16", ctx_params=(64, 0, 33)),
+    # G x slices = 16 (4 slices of a 64-token prefix; 8 of a 128-token one at G = 2): the
+    # suffix pass takes the prefix partials into LDS at a segment's first piece.  (The
+    # cases above with G x slices > 16 or G > 4 fold them from memory.)
+    "fp8-lds-fold": PREFIX.replace(num_seqs=9, prefix_groups=2, kv_dtype="fp8", ctx_params=(64, 0, 70)),
+    "g2-lds-fold": PREFIX.replace(num_seqs=5, num_q_heads=16, num_kv_heads=8, block_size=16,
+                                  ctx_params=(128, 0, 40)),
 }
 
 
