@@ -77,6 +77,8 @@ def parse_args():
                     help="only run a plain 1 GiB device copy --steps times (counter calibration)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the chunked-prefill leg (--reps calls) and print its result")
+    ap.add_argument("--blocks-only", action="store_true",
+                    help="only run the block-moves leg (--reps calls each) and print its result")
     return ap.parse_args()
 
 
@@ -482,9 +484,14 @@ def measure_block_moves(args):
     vh = torch.empty((n,) + tuple(shape[1:]), dtype=torch.bfloat16, pin_memory=True)
     flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
+    # the practical ceiling of a move: one contiguous device copy of the same bytes (2n
+    # whole blocks), no block lookup
+    csrc = k[:2 * n]
+    cdst = torch.empty_like(csrc)
     out = {}
     for name, call in (("copy_blocks", lambda: pkv.paged_kv_copy_blocks(src, dst, k, v)),
                        ("swap_out_to_device", lambda: pkv.paged_kv_swap_out(src, k, v, kb, vb)),
+                       ("contiguous_device_copy", lambda: cdst.copy_(csrc)),
                        ("swap_out_to_pinned_host", lambda: pkv.paged_kv_swap_out(src, k, v, kh, vh)),
                        ("swap_in_from_pinned_host", lambda: pkv.paged_kv_swap_in(dst, kh, vh, k, v))):
         for _ in range(3):
@@ -509,6 +516,8 @@ def measure_block_moves(args):
                      "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log(f"[block moves] {name}: {n} blocks of {block_bytes} B (K and V), {ms * 1e3:.1f} us, "
             f"{out[name]['GBps']:.0f} GB/s read+write ({100 * out[name]['frac_hbm_peak']:.1f}% of peak)")
+    for name in ("copy_blocks", "swap_out_to_device"):
+        out[name]["frac_of_contiguous_copy"] = out[name]["GBps"] / out["contiguous_device_copy"]["GBps"]
     return out
 
 
@@ -705,7 +714,7 @@ def main():
               "no multi-GPU leg (a decode step shards by KV head or by sequence, with no collective "
               "inside the step)", file=sys.stderr)
         sys.exit(2)
-    clocks = gpu_clocks() if not args.copy_calibration and not args.prefill_only else None
+    clocks = gpu_clocks() if not (args.copy_calibration or args.prefill_only or args.blocks_only) else None
     import torch
     import paged_kv_cache_27_amd as pkv
 
@@ -725,6 +734,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps(measure_prefill(args)))
+        return
+    if args.blocks_only:
+        print(json.dumps(measure_block_moves(args)))
         return
     from workloads import CONFIGS, EXTRA_CONFIGS
     cfg = pick_config(args.config)

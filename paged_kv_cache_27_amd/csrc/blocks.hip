@@ -12,8 +12,14 @@
 //     (same page, section "Estrategia 2: swap": an evicted session's blocks go to CPU
 //     RAM and come back when it resumes).  The buffer may be device memory or pinned
 //     host memory (then the kernel's stores and loads cross PCIe).
-// One workgroup moves one block of one cache with 16-byte accesses, four in flight per
-// thread.  An ID outside [0, num_blocks) skips its pair or row.
+// One workgroup moves one block of one cache with 16-byte accesses: every load of a
+// thread's share is issued before its first store (eight per thread for a 32 KiB block),
+// so a block costs one memory round trip.  Loads take the streaming (nontemporal) cache
+// policy -- a moved block is not read again by this kernel -- and stores the ordinary
+// one.  (Measured on the 2 048-block moves of the 8B-shaped cache: four loads in flight,
+// both policies ordinary, 53 us for a copy-on-write; eight in flight 45 us; streaming
+// loads 42 us, against 48 us for one contiguous device copy of the same bytes; streaming
+// stores as well 58 us.)  An ID outside [0, num_blocks) skips its pair or row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,6 +28,8 @@
 namespace pkv {
 
 constexpr int kMoveThreads = 256;
+constexpr int kMoveUnroll = 8;  // 16-byte loads in flight per thread
+typedef uint32_t move16_t __attribute__((ext_vector_type(4)));
 
 // src / dst: base addresses; a null ID array means "row i of a contiguous buffer".
 __global__ void __launch_bounds__(kMoveThreads)
@@ -32,19 +40,19 @@ move_blocks_kernel(const uint8_t* k_src, const uint8_t* v_src, const int32_t* sr
   const int64_t d = dst_ids ? (int64_t)dst_ids[i] : i;
   // IDs address the cache side; buffer rows i < num are always in range
   if (s < 0 || d < 0 || (src_ids && s >= num_blocks) || (dst_ids && d >= num_blocks)) return;
-  const uint4* from = (const uint4*)((blockIdx.y == 0 ? k_src : v_src) + s * block_bytes);
-  uint4* to = (uint4*)((blockIdx.y == 0 ? k_dst : v_dst) + d * block_bytes);
+  const move16_t* from = (const move16_t*)((blockIdx.y == 0 ? k_src : v_src) + s * block_bytes);
+  move16_t* to = (move16_t*)((blockIdx.y == 0 ? k_dst : v_dst) + d * block_bytes);
   const int64_t n = block_bytes / 16;
-  constexpr int U = 4;
+  constexpr int U = kMoveUnroll;
   int64_t e = threadIdx.x;
   for (; e + (U - 1) * kMoveThreads < n; e += U * kMoveThreads) {
-    uint4 x[U];
+    move16_t x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = from[e + u * kMoveThreads];
+    for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(from + e + u * kMoveThreads);
 #pragma unroll
     for (int u = 0; u < U; ++u) to[e + u * kMoveThreads] = x[u];
   }
-  for (; e < n; e += kMoveThreads) to[e] = from[e];
+  for (; e < n; e += kMoveThreads) to[e] = __builtin_nontemporal_load(from + e);
 }
 
 hipError_t launch_move_blocks(const void* k_src, const void* v_src, const int32_t* src_ids, void* k_dst,
