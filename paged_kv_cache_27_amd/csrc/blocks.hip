@@ -23,15 +23,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_device.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 
 constexpr int kMoveThreads = 256;
 constexpr int kMoveUnroll = 8;  // 16-byte loads in flight per thread
-typedef uint32_t move16_t __attribute__((ext_vector_type(4)));
 
 // src / dst: base addresses; a null ID array means "row i of a contiguous buffer".
+// Whole rounds of kMoveUnroll pieces per thread use plain global accesses; the last,
+// partial round of a block that is not a multiple of kMoveUnroll * kMoveThreads pieces
+// goes through buffer resources that cover exactly the source and destination block,
+// so its pieces past the block's end load zeros and store nothing, without a branch.
+// (Buffer accesses for every round measured 0.6-0.9 us slower on 32 KiB blocks.)
+typedef uint32_t move16_t __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(kMoveThreads)
 move_blocks_kernel(const uint8_t* k_src, const uint8_t* v_src, const int32_t* src_ids, uint8_t* k_dst,
                    uint8_t* v_dst, const int32_t* dst_ids, int64_t block_bytes, int64_t num_blocks) {
@@ -40,24 +46,34 @@ move_blocks_kernel(const uint8_t* k_src, const uint8_t* v_src, const int32_t* sr
   const int64_t d = dst_ids ? (int64_t)dst_ids[i] : i;
   // IDs address the cache side; buffer rows i < num are always in range
   if (s < 0 || d < 0 || (src_ids && s >= num_blocks) || (dst_ids && d >= num_blocks)) return;
-  const move16_t* from = (const move16_t*)((blockIdx.y == 0 ? k_src : v_src) + s * block_bytes);
-  move16_t* to = (move16_t*)((blockIdx.y == 0 ? k_dst : v_dst) + d * block_bytes);
-  const int64_t n = block_bytes / 16;
+  const uint8_t* from = (blockIdx.y == 0 ? k_src : v_src) + s * block_bytes;
+  uint8_t* to = (blockIdx.y == 0 ? k_dst : v_dst) + d * block_bytes;
+  const int n = (int)(block_bytes / 16);  // pieces; block_bytes < 2^31, checked by the launcher
   constexpr int U = kMoveUnroll;
-  int64_t e = threadIdx.x;
+  int e = threadIdx.x;
   for (; e + (U - 1) * kMoveThreads < n; e += U * kMoveThreads) {
     move16_t x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(from + e + u * kMoveThreads);
+    for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load((const move16_t*)from + e + u * kMoveThreads);
 #pragma unroll
-    for (int u = 0; u < U; ++u) to[e + u * kMoveThreads] = x[u];
+    for (int u = 0; u < U; ++u) ((move16_t*)to)[e + u * kMoveThreads] = x[u];
   }
-  for (; e < n; e += kMoveThreads) to[e] = __builtin_nontemporal_load(from + e);
+  if (e - (int)threadIdx.x >= n) return;  // every piece of this thread came in whole rounds
+  const __amdgpu_buffer_rsrc_t rf = tile_rsrc(from, (int)block_bytes);
+  const __amdgpu_buffer_rsrc_t rt = tile_rsrc(to, (int)block_bytes);
+  u32x4_t x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    x[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rf, 16 * (e + u * kMoveThreads), 0, kAuxNT));
+#pragma unroll
+  for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(x[u], rt, 16 * (e + u * kMoveThreads), 0, 0);
 }
 
 hipError_t launch_move_blocks(const void* k_src, const void* v_src, const int32_t* src_ids, void* k_dst,
                               void* v_dst, const int32_t* dst_ids, int32_t num, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream) {
+  if (block_bytes <= 0 || block_bytes >= ((int64_t)1 << 31) - 16 * kMoveUnroll * kMoveThreads)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(move_blocks_kernel, dim3((unsigned)num, 2), dim3(kMoveThreads), 0, stream,
                      (const uint8_t*)k_src, (const uint8_t*)v_src, src_ids, (uint8_t*)k_dst,
                      (uint8_t*)v_dst, dst_ids, block_bytes, num_blocks);

@@ -10,7 +10,7 @@ import torch
 import paged_kv_cache_27_amd as pkv
 from gpu_helpers import GpuStep, assert_close_to_oracle, cache_bytes, out_to_f64, to_device
 from helpers import oracle_step
-from workloads import LLAMA8B, R70B_FP8, make_workload
+from workloads import LLAMA8B, R70B_FP8, TINY, make_workload
 
 pytestmark = pytest.mark.gpu
 THREADS = min(16, len(os.sched_getaffinity(0)))
@@ -56,10 +56,21 @@ def _pool_for(w):
     return pool
 
 
-@pytest.mark.parametrize("cfg", [LLAMA8B.replace(num_seqs=3, ctx_params=(40, 300)),
-                                 R70B_FP8.replace(num_seqs=3, ctx_params=(200, 0.5, 16, 400))],
-                         ids=["bf16", "fp8"])
-def test_copy_blocks_bit_exact(orc, cfg):
+# Block geometries: 32 KiB (whole rounds of the move kernel's 8 x 256 16-byte pieces), 16
+# KiB fp8 and 12 KiB fp32 (a partial round only), 40 KiB (a whole round, then a partial
+# one) and 96 KiB (three whole rounds).
+COPY_CASES = {
+    "bf16": LLAMA8B.replace(num_seqs=3, ctx_params=(40, 300)),
+    "fp8": R70B_FP8.replace(num_seqs=3, ctx_params=(200, 0.5, 16, 400)),
+    "f32-12k": TINY.replace(num_kv_heads=3, num_q_heads=6, pool_blocks=0),
+    "bf16-40k": LLAMA8B.replace(num_seqs=3, num_kv_heads=5, num_q_heads=20, block_size=32, ctx_params=(40, 300)),
+    "bf16-96k": LLAMA8B.replace(num_seqs=3, num_kv_heads=12, num_q_heads=24, block_size=32, ctx_params=(40, 300)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(COPY_CASES))
+def test_copy_blocks_bit_exact(orc, name):
+    cfg = COPY_CASES[name]
     w, g, kc, vc = _prepared(orc, cfg)
     rng = np.random.default_rng(5)
     live, free = _live_blocks(w), [b for b in range(w.num_blocks) if b not in set(_live_blocks(w))]
@@ -76,7 +87,7 @@ def test_copy_blocks_bit_exact(orc, cfg):
     _assert_caches_equal(g, kc, vc, "copy_blocks")
 
 
-SWAP_CASES = [("bf16", "device"), ("bf16", "pinned-host"), ("fp8", "pinned-host")]
+SWAP_CASES = [("bf16", "device"), ("bf16", "pinned-host"), ("fp8", "pinned-host"), ("bf16-40k", "pinned-host")]
 
 
 @pytest.mark.parametrize("kv,where", SWAP_CASES, ids=[f"{k}-{w}" for k, w in SWAP_CASES])
@@ -85,9 +96,12 @@ def test_swap_round_trip(orc, kv, where):
     moves the blocks across the host link: "Estrategia 2: swap" keeps an evicted session
     in CPU RAM), byte-compared with the oracle's swap-out; then swap in from the same
     buffers to other blocks, caches compared byte for byte."""
-    base = LLAMA8B if kv == "bf16" else R70B_FP8.replace(ctx_params=(100, 0.5, 16, 300))
-    cfg = base.replace(num_seqs=2, pool_factor=3.0) if kv == "fp8" else \
-        base.replace(num_seqs=2, ctx_params=(64, 200), pool_factor=3.0)
+    if kv == "fp8":
+        cfg = R70B_FP8.replace(ctx_params=(100, 0.5, 16, 300), num_seqs=2, pool_factor=3.0)
+    elif kv == "bf16-40k":  # a block of one whole and one partial round of the move kernel
+        cfg = COPY_CASES[kv].replace(num_seqs=2, ctx_params=(64, 200), pool_factor=3.0)
+    else:
+        cfg = LLAMA8B.replace(num_seqs=2, ctx_params=(64, 200), pool_factor=3.0)
     w, g, kc, vc = _prepared(orc, cfg)
     live = _live_blocks(w)
     free = [b for b in range(w.num_blocks) if b not in set(live)]
