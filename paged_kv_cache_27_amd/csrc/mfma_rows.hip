@@ -35,7 +35,13 @@
 //   * V's B operand needs those 8 tokens of one dim per lane: the workgroup stages each
 //     step's V once in LDS as [lane group][dim][8 tokens], so a lane's fragment is one
 //     conflict-free 16-byte LDS read (again serving both sets);
-//   * the row sums come from the same P times a tile of ones.
+//   * the row sums come from the same weights in fp32, on the VALU: each lane adds its 8
+//     weights of row l%16 into a running share (rescaled with the row), and the four lane
+//     groups' shares are summed once at the end.  (As P times a tile of ones on the
+//     matrix cores -- two more MFMAs per row set and step -- prefill over a 16-bit cache
+//     measured ~1-2 % slower.)  Prefill over an fp8 cache keeps the ones tile: there the
+//     VALU sums cost the registers of a third wave per SIMD (174 against 167 VGPRs), and
+//     it measured 4 % slower with them.
 // Two row sets per wave halve the LDS reads, staging and barriers per MFMA against one
 // set, and give each wave two independent softmax chains (measured 9% faster on the
 // chunked-prefill workload at ~170 VGPRs, two waves per SIMD, than one set at ~110 VGPRs
@@ -242,18 +248,22 @@ rows_kernel(const RowsArgs a) {
                              : 16 * c1;
 
   // per set: m, the row's reference max (log2 domain, scaled); O, unnormalised output
-  // rows 4(l/16) + i, dims 16jj + l%16; Ol, the same rows' denominators, summed on the
-  // matrix cores as P times a ones tile (every column holds the row sum)
+  // rows 4(l/16) + i, dims 16jj + l%16; lrow, this lane's share of row l%16's denominator
+  // (VSUM), or Om, the denominators of rows 4(l/16) + i summed on the matrix cores as P
+  // times a ones tile (every column holds the row sum)
+  constexpr bool VSUM = !(PREFILL && KV == kFP8);
   float m[RS];
-  f32x4_t O[RS][NJ], Ol[RS];
+  f32x4_t O[RS][NJ];
+  float lrow[RS];
+  f32x4_t Om[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     m[rs] = kNegInf;
-    Ol[rs] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    lrow[rs] = 0.0f;
+    Om[rs] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) O[rs][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  const frag8 ones = __builtin_bit_cast(frag8, make_uint4(O_::kOne, O_::kOne, O_::kOne, O_::kOne));
 
   const int bs_shift = BS == 32 ? 5 : 4;  // block size 16 or 32
   // A step's two chunks (clamped to the range's last one): their physical blocks, read
@@ -424,11 +434,12 @@ rows_kernel(const RowsArgs a) {
         const float mn = move[rs] ? bm[rs] : m[rs];
         const float alpha = fast_exp2(m[rs] - mn);  // 0 on the first step, 1 for rows kept
         m[rs] = mn;
+        if constexpr (VSUM) lrow[rs] *= alpha;  // this lane's row is row l%16
         // O rows 4(l/16) + i take the factor of row 4(l/16) + i, held by lane 4(l/16) + i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ai = __shfl(alpha, 4 * (lane >> 4) + i);
-          Ol[rs][i] *= ai;
+          if constexpr (!VSUM) Om[rs][i] *= ai;
 #pragma unroll
           for (int jj = 0; jj < NJ; ++jj) O[rs][jj][i] *= ai;
         }
@@ -445,8 +456,13 @@ rows_kernel(const RowsArgs a) {
       for (int i = 0; i < 4; ++i) O_::split2(p[2 * i], p[2 * i + 1], hw[i], lw[i]);
       ahi[rs] = __builtin_bit_cast(frag8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
       alo[rs] = __builtin_bit_cast(frag8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      Ol[rs] = O_::qk(ahi[rs], ones, Ol[rs]);
-      Ol[rs] = O_::qk(alo[rs], ones, Ol[rs]);
+      if constexpr (VSUM) {
+        lrow[rs] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      } else {
+        const frag8 ones = __builtin_bit_cast(frag8, make_uint4(O_::kOne, O_::kOne, O_::kOne, O_::kOne));
+        Om[rs] = O_::qk(ahi[rs], ones, Om[rs]);
+        Om[rs] = O_::qk(alo[rs], ones, Om[rs]);
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
@@ -491,6 +507,23 @@ rows_kernel(const RowsArgs a) {
     }
   }
 
+  // each row's denominator: the four lane groups' shares summed (every lane of column l%16
+  // then holds row l%16's), and Ol[rs][i] that of row 4(l/16) + i, the layout of O
+  f32x4_t Ol[RS];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    if constexpr (!VSUM) {
+      Ol[rs] = Om[rs];
+      continue;
+    }
+    float x = lrow[rs];
+    auto r16 = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
+    x = bits_f32(r16[0]) + bits_f32(r16[1]);
+    auto r32 = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+    x = bits_f32(r32[0]) + bits_f32(r32[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ol[rs][i] = __shfl(x, 4 * (lane >> 4) + i);
+  }
   if constexpr (PREFILL) {
     // ---- output rows 4(l/16) + i of each set, dims 16jj + l%16: acc / l of that row,
     // rounded to the output dtype
