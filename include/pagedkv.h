@@ -331,7 +331,7 @@ int paged_attention_prefill(const void* q, pkv_dtype q_dtype, int32_t num_seqs, 
  * Whole physical blocks of one layer's K and V caches (block_bytes = num_kv_heads *
  * block_size * head_dim * element bytes each).  IDs are int32 device arrays; an ID
  * outside [0, num_blocks) skips its pair or row.  Asynchronous on `stream`; no
- * allocation.
+ * allocation.  A block of 2^31 - 32768 bytes or more returns PKV_ERR_SHAPE.
  *
  * Copy-on-write: block src_ids[i] -> block dst_ids[i] in both caches, so a sequence
  * about to write into a block it shares gets a private copy first ("PagedAttention por

@@ -427,7 +427,7 @@ int paged_kv_copy_blocks(const int32_t* src_ids, const int32_t* dst_ids, int32_t
                          void* k_cache, void* v_cache, const pkv_cache_desc* cache, hipStream_t stream) {
   int st = check_cache(cache);
   if (st) return st;
-  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs < 0 || block_bytes(cache) >= pkv::kMoveMaxBlockBytes) return PKV_ERR_SHAPE;
   if (num_pairs == 0) return PKV_OK;
   if (!src_ids || !dst_ids || !k_cache || !v_cache) return PKV_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_SHAPE;
@@ -440,7 +440,7 @@ int paged_kv_swap_out(const int32_t* ids, int32_t num, const void* k_cache, cons
                       const pkv_cache_desc* cache, void* k_buf, void* v_buf, hipStream_t stream) {
   int st = check_cache(cache);
   if (st) return st;
-  if (num < 0) return PKV_ERR_SHAPE;
+  if (num < 0 || block_bytes(cache) >= pkv::kMoveMaxBlockBytes) return PKV_ERR_SHAPE;
   if (num == 0) return PKV_OK;
   if (!ids || !k_cache || !v_cache || !k_buf || !v_buf) return PKV_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
@@ -456,7 +456,7 @@ int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const v
                      void* k_cache, void* v_cache, const pkv_cache_desc* cache, hipStream_t stream) {
   int st = check_cache(cache);
   if (st) return st;
-  if (num < 0) return PKV_ERR_SHAPE;
+  if (num < 0 || block_bytes(cache) >= pkv::kMoveMaxBlockBytes) return PKV_ERR_SHAPE;
   if (num == 0) return PKV_OK;
   if (!ids || !k_cache || !v_cache || !k_buf || !v_buf) return PKV_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))

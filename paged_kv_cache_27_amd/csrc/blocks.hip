@@ -72,8 +72,8 @@ move_blocks_kernel(const uint8_t* k_src, const uint8_t* v_src, const int32_t* sr
 hipError_t launch_move_blocks(const void* k_src, const void* v_src, const int32_t* src_ids, void* k_dst,
                               void* v_dst, const int32_t* dst_ids, int32_t num, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream) {
-  if (block_bytes <= 0 || block_bytes >= ((int64_t)1 << 31) - 16 * kMoveUnroll * kMoveThreads)
-    return hipErrorInvalidValue;
+  static_assert(16 * kMoveUnroll * kMoveThreads <= ((int64_t)1 << 31) - kMoveMaxBlockBytes, "round headroom");
+  if (block_bytes <= 0 || block_bytes >= kMoveMaxBlockBytes) return hipErrorInvalidValue;
   hipLaunchKernelGGL(move_blocks_kernel, dim3((unsigned)num, 2), dim3(kMoveThreads), 0, stream,
                      (const uint8_t*)k_src, (const uint8_t*)v_src, src_ids, (uint8_t*)k_dst,
                      (uint8_t*)v_dst, dst_ids, block_bytes, num_blocks);

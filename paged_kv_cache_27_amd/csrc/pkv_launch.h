@@ -95,6 +95,7 @@ hipError_t launch_prefill(const RowsArgs& a);
 // dst_ids is null) of the destinations; a negative ID skips the pair.
 // An ID array's entries address blocks [0, num_blocks) of that side's cache; the others
 // are skipped.  A null ID array means row i of a contiguous buffer.
+constexpr int64_t kMoveMaxBlockBytes = ((int64_t)1 << 31) - 32768;  // 32-bit offsets with a round's headroom
 hipError_t launch_move_blocks(const void* k_src, const void* v_src, const int32_t* src_ids, void* k_dst,
                               void* v_dst, const int32_t* dst_ids, int32_t num, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream);

@@ -288,6 +288,13 @@ def test_block_move_argument_errors():
     assert copy(FAKE, FAKE, 3, mis, FAKE, d, None) == -3
     assert copy(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(_desc(dtype=7)), None) == -2
     assert copy(FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(_desc(block_size=8)), None) == -3
+    # blocks of 2^31 - 32768 bytes or more (the move kernel's 32-bit offsets) are refused
+    huge = ctypes.byref(_desc(num_kv_heads=65536, block_size=32, head_dim=128, dtype=pkv.F32))  # 1 GiB blocks: fine
+    big = ctypes.byref(_desc(num_kv_heads=131072, block_size=32, head_dim=128, dtype=pkv.F32))  # 2 GiB
+    assert copy(FAKE, FAKE, 3, FAKE, FAKE, big, None) == -3
+    assert out(FAKE, 2, FAKE, FAKE, big, FAKE, FAKE, None) == -3
+    assert into(FAKE, 2, FAKE, FAKE, FAKE, FAKE, big, None) == -3
+    assert copy(None, FAKE, 3, FAKE, FAKE, huge, None) == -1  # passes the size check
     for f, args in ((out, lambda n, buf: (FAKE, n, FAKE, FAKE, d, buf, FAKE, None)),
                     (into, lambda n, buf: (FAKE, n, buf, FAKE, FAKE, FAKE, d, None))):
         assert f(*args(-1, FAKE)) == -3
