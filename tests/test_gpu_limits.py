@@ -8,7 +8,8 @@ oracle within the decode bar (4e-3 * max(1, |ref|)):
 * one 262 144-token context: in the balanced schedule a single segment spans every
   workgroup, so the last workgroup to finish combines one partial from each of them; in
   512-token partitions the merge kernel combines 512 partials; in one pass a single
-  workgroup per KV head streams it all.
+  workgroup per KV head streams it all;
+* shared-prefix decode of 8 191 sequences, and a single 4 096-token prefill chunk.
 
 The schedule each case runs is checked first, so a change of the planning rules cannot
 silently move a case off the path it is meant to cover.
@@ -70,3 +71,48 @@ def test_longest_context(orc, partition, schedule):
     cfg = LLAMA8B.replace(name="limits-256k-context", num_seqs=1, num_q_heads=4, num_kv_heads=1,
                           ctx_kind="fixed", ctx_params=(262144,), seed=262144)
     _check(orc, cfg, partition, schedule)
+
+
+def test_shared_prefix_most_sequences(orc):
+    """8 191 sequences on one shared prefix: the suffix pass's per-sequence LDS arrays at
+    their largest beside its prefix-partial tiles."""
+    from workloads import PREFIX
+    cfg = PREFIX.replace(name="limits-prefix-8191-seqs", num_seqs=8191, num_q_heads=4, num_kv_heads=1,
+                         ctx_params=(64, 0, 20), seed=18191)
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    starts = torch.from_numpy(np.asarray(w.prefix_group_starts(), np.int32)).cuda()
+    pl = torch.full((cfg.num_seqs,), 64, dtype=torch.int32, device="cuda")
+    print(f"limits case {cfg.name}: N={cfg.num_seqs} groups={list(w.prefix_group_starts())}", flush=True)
+    pkv.paged_attention_decode_shared_prefix(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens, w.scale,
+                                             g.out, w.max_context_len, starts, pl, cfg.num_seqs, 64,
+                                             kv_dtype=g.kv_dtype)
+    torch.cuda.synchronize()
+    _, _, _, ref = oracle_step(orc, w, threads=THREADS)
+    assert_close_to_oracle(out_to_f64(g.out), ref, cfg.kv_dtype, cfg.name)
+
+
+def test_prefill_whole_4096_token_prompt(orc):
+    """One 4 096-token chunk, the whole prompt (32 row tiles of 128 rows per KV head)."""
+    from gpu_helpers import to_device, torch_dtype
+    from workloads import prefill_queries
+    cfg = LLAMA8B.replace(name="limits-prefill-4096", num_seqs=1, num_q_heads=4, num_kv_heads=1,
+                          ctx_kind="fixed", ctx_params=(4096,), seed=4096)
+    w = make_workload(cfg)
+    g = GpuStep(w)
+    g.fill_history()
+    g.write_new()
+    q, cu = prefill_queries(w, (4096,), 11)
+    out = torch.empty((4096, cfg.num_q_heads, cfg.head_dim), dtype=torch_dtype(cfg.out_dtype), device="cuda")
+    print(f"limits case {cfg.name}: one 4096-token chunk", flush=True)
+    pkv.paged_attention_prefill(to_device(q, cfg.q_dtype), torch.from_numpy(cu).cuda(), 4096, g.k_cache, g.v_cache,
+                                g.block_tables, g.context_lens, w.scale, out, w.max_context_len)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    del g
+    kc, vc, _, _ = oracle_step(orc, w, pairs=np.zeros((0, 2), np.int32))
+    ref = orc.prefill(q, cfg.q_dtype, cu, kc, vc, cfg.kv_dtype, w.block_tables, w.context_lens, w.scale,
+                      w.k_scale, w.v_scale, threads=THREADS)
+    assert_close_to_oracle(got, ref, cfg.kv_dtype, cfg.name)
