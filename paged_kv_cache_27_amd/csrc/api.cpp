@@ -331,7 +331,10 @@ __global__ void zero_words_kernel(uint32_t* p, int n) {
 }
 
 // The current device's scratch address; on its first use the counter header is cleared
-// on `stream` (a fill kernel), and every decode leaves it zero after that.
+// on `stream` (a fill kernel), and every decode leaves it zero after that.  A first use
+// under stream capture only records the fill into the graph (it runs at each replay,
+// before the decode recorded after it), so the device is not marked cleared until a
+// call outside capture has launched the fill itself.
 int scratch_for_current_device(hipStream_t stream, void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
@@ -346,6 +349,11 @@ int scratch_for_current_device(hipStream_t stream, void** out) {
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
   if (!ptr) {
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+      (void)hipGetLastError();
+      return PKV_ERR_LAUNCH;
+    }
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
       (void)hipGetLastError();
       return PKV_ERR_LAUNCH;
@@ -353,7 +361,7 @@ int scratch_for_current_device(hipStream_t stream, void** out) {
     constexpr int kWords = (int)(pkv::kWsHeaderBytes / sizeof(uint32_t));
     hipLaunchKernelGGL(zero_words_kernel, dim3(kWords / 256), dim3(256), 0, stream, (uint32_t*)ptr, kWords);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
-    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    if (capture == hipStreamCaptureStatusNone) g_scratch_ptr[dev].store(ptr, std::memory_order_release);
   }
   *out = ptr;
   return PKV_OK;
