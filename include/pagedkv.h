@@ -355,11 +355,112 @@ int paged_kv_copy_blocks(const int32_t* src_ids, const int32_t* dst_ids, int32_t
  * launch.  Release the swapped-out blocks to the pool only
  * after the stream has finished the swap out, and decode from swapped-in blocks only
  * on the same stream after the swap in (or after synchronising with it).
+ * Precondition of swap in (unchecked): its IDs distinct.
  */
 int paged_kv_swap_out(const int32_t* ids, int32_t num, const void* k_cache, const void* v_cache,
                       const pkv_cache_desc* cache, void* k_buf, void* v_buf, hipStream_t stream);
 int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const void* v_buf,
                      void* k_cache, void* v_cache, const pkv_cache_desc* cache, hipStream_t stream);
+
+/* --------------------------------------------------------------- input checks ---
+ * Debugging aids for the preconditions that the calls above leave unchecked on the
+ * device (a call that breaks one reads or writes memory the caller did not mean, or
+ * races).  Each check reads only the index arrays it is given -- never a cache -- within
+ * the bounds its size arguments give, and reports into `result`, a pkv_check_result in
+ * device memory (8-byte aligned) that the check initialises itself: three kernels in
+ * order on `stream`, no memset, no allocation, no synchronisation, so `result` is valid
+ * once the stream has passed the call.  Host-visible argument errors return before
+ * anything is launched: PKV_ERR_NULL for a NULL result or a NULL array the check reads,
+ * PKV_ERR_SHAPE for negative sizes, the bounds the checked call refuses (a table row
+ * shorter than max_context_len, max_q_len above it, the shared-prefix bounds), or a
+ * result that is misaligned or not device memory.  Cost: linear in the entries checked, except the
+ * duplicate rules, which compare every pair of entries (quadratic in num_tokens or num
+ * pairs: a debugging aid, not for the hot path).
+ *
+ * A violation is one (entry, rule) pair.  `violations` counts them; `code` is the lowest
+ * code violated and `index` the lowest index violating it (what an index counts is
+ * given per code).  With no violation, code is PKV_CHECK_OK and index -1.
+ */
+typedef enum {
+  PKV_CHECK_OK = 0,
+  PKV_CHECK_DUPLICATE_SLOT = 1, /* token t: writes a cache slot an earlier token writes */
+  PKV_CHECK_SEQ_ID = 2,         /* token t: seq_ids[t] >= num_seqs */
+  PKV_CHECK_CONTEXT_LEN = 3,    /* sequence s: context_lens[s] < 0 or > max_context_len */
+  PKV_CHECK_BLOCK_ID = 4,       /* table entry s * max_blocks_per_seq + j read by the call: ID
+                                   outside [0, num_blocks) */
+  PKV_CHECK_GROUP_STARTS = 5,   /* entry j of group_starts, 0 <= j <= num_groups */
+  PKV_CHECK_PREFIX_LEN = 6,     /* sequence s: prefix_lens[s] */
+  PKV_CHECK_PREFIX_BLOCKS = 7,  /* table entry s * max_blocks_per_seq + j: a prefix block that
+                                   differs from the group's first sequence's */
+  PKV_CHECK_QUERY_ROWS = 8,     /* sequence s: its query rows in cu_q */
+  PKV_CHECK_BLOCK_PAIR = 9      /* pair or row i: destination repeated, or equal to a source */
+} pkv_check_code;
+
+typedef struct {
+  int32_t code;       /* pkv_check_code */
+  int32_t reserved;   /* 0 after the check */
+  int64_t index;      /* -1 when code is PKV_CHECK_OK */
+  int64_t violations;
+} pkv_check_result;
+
+/* paged_kv_write: token t is *active* when 0 <= slot_mapping[t] < num_blocks * B (the
+ * others write nothing).  DUPLICATE_SLOT: active t whose slot an earlier active token
+ * has too. */
+int paged_kv_check_slots(const int64_t* slot_mapping, int32_t num_tokens, const pkv_cache_desc* cache,
+                         pkv_check_result* result, hipStream_t stream);
+
+/* paged_kv_slot_mapping and paged_kv_write_positions.  SEQ_ID: token t with
+ * seq_ids[t] >= num_seqs.  DUPLICATE_SLOT: as paged_kv_check_slots over the slots the
+ * other tokens resolve to (by the rule of paged_kv_slot_mapping; block_tables is
+ * [num_seqs][max_blocks_per_seq]). */
+int paged_kv_check_positions(const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                             int32_t num_seqs, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const pkv_cache_desc* cache, pkv_check_result* result, hipStream_t stream);
+
+/* paged_attention_decode, _noalloc (window = sinks = 0) and _window.  CONTEXT_LEN:
+ * sequence s with context_lens[s] outside [0, max_context_len].  BLOCK_ID: for every
+ * other sequence, entry j of its table row is read when block j holds an attended token
+ * (any of its first context_lens[s] tokens; with window > 0, positions >=
+ * context_lens[s] - window or < sinks); a read entry outside [0, num_blocks) is a
+ * violation. */
+int paged_attention_check_decode(int32_t num_seqs, const pkv_cache_desc* cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, int32_t window, int32_t sinks,
+                                 pkv_check_result* result, hipStream_t stream);
+
+/* paged_attention_decode_shared_prefix: the decode rules (window 0), plus
+ * GROUP_STARTS: entry j outside [0, num_seqs], entry 0 not 0, entry num_groups not
+ * num_seqs, or (j < num_groups) group j's size group_starts[j+1] - group_starts[j]
+ * negative or above max_group_size.  When group_starts breaks no rule (every sequence
+ * then lies in one group, whose first sequence is f):
+ * PREFIX_LEN: sequence s whose prefix_lens[s] is negative, not a multiple of B, above
+ * max_prefix_len or context_lens[s], or unequal to prefix_lens[f];
+ * PREFIX_BLOCKS: entry j < prefix_lens[f] / B of a sequence s != f that differs from
+ * entry j of f's row (checked when prefix_lens[f] is non-negative, a multiple of B and
+ * at most max_prefix_len).  Host-side errors as for the call (num_groups, bounds). */
+int paged_attention_check_shared_prefix(int32_t num_seqs, const pkv_cache_desc* cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        const int32_t* group_starts, int32_t num_groups,
+                                        int32_t max_group_size, const int32_t* prefix_lens,
+                                        int32_t max_prefix_len, pkv_check_result* result,
+                                        hipStream_t stream);
+
+/* paged_attention_prefill: CONTEXT_LEN as for decode.  QUERY_ROWS: sequence s whose
+ * n_s = cu_q[s+1] - cu_q[s] is negative, above max_q_len or above context_lens[s], and
+ * s = 0 when cu_q[0] != 0.  BLOCK_ID: a sequence breaking neither rule and with n_s >= 1
+ * reads entries j < ceil(context_lens[s] / B). */
+int paged_attention_check_prefill(int32_t num_seqs, const int32_t* cu_q, int32_t max_q_len,
+                                  const pkv_cache_desc* cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, pkv_check_result* result, hipStream_t stream);
+
+/* paged_kv_copy_blocks (src_ids, dst_ids) and paged_kv_swap_in (src_ids NULL, dst_ids =
+ * its ids).  Pair i is *active* when dst_ids[i] and (if given) src_ids[i] lie in [0,
+ * num_blocks) (the others move nothing).  BLOCK_PAIR: active i whose destination an
+ * earlier active pair has too, or equals the source of any active pair (itself included). */
+int paged_kv_check_block_ids(const int32_t* src_ids, const int32_t* dst_ids, int32_t num,
+                             const pkv_cache_desc* cache, pkv_check_result* result, hipStream_t stream);
 
 /* ----------------------------------------------------------------- block pool ---
  * Host-side refcounted free list of one cache's physical blocks ("PagedAttention por

@@ -30,7 +30,9 @@ EXPORTED = ["paged_kv_slot_mapping", "paged_kv_write", "paged_kv_write_positions
             "paged_attention_prefill", "paged_kv_copy_blocks", "paged_kv_swap_out", "paged_kv_swap_in",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_alloc", "pkv_pool_share", "pkv_pool_release",
             "pkv_pool_cow", "pkv_pool_free_count", "pkv_pool_refcount",
-            "pkv_status_string", "pkv_abi_version"]
+            "pkv_status_string", "pkv_abi_version",
+            "paged_kv_check_slots", "paged_kv_check_positions", "paged_attention_check_decode",
+            "paged_attention_check_shared_prefix", "paged_attention_check_prefill", "paged_kv_check_block_ids"]
 SCHEDULES = {0: "single-pass", 1: "fixed-partitions", 2: "balanced"}
 
 
@@ -167,6 +169,16 @@ def _stream(stream) -> int | None:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _debug(fn: str, check: str, *args, **kw) -> None:
+    """Debug mode (PAGEDKV_DEBUG set, not 0): run the library's input check for `fn` first
+    and raise PreconditionError instead of launching when an entry breaks a rule."""
+    import os
+    if os.environ.get("PAGEDKV_DEBUG", "") in ("", "0"):
+        return
+    from . import _checks
+    _checks.raise_if_broken(fn, getattr(_checks, check)(*args, **kw))
+
+
 def dtype_code(x) -> int:
     if isinstance(x, str):
         return _NAME_CODES[x]
@@ -221,6 +233,7 @@ def paged_kv_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    k_scale: float = 1.0, v_scale: float = 1.0, src_dtype=None,
                    stream=None) -> None:
     lib = load_library()
+    _debug("paged_kv_write", "paged_kv_check_slots", slot_mapping, k_cache, kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
     assert slot_mapping.dtype == torch.int64
     src = dtype_code(src_dtype if src_dtype is not None else k.dtype)
@@ -236,6 +249,8 @@ def paged_kv_write_positions(seq_ids: torch.Tensor, positions: torch.Tensor, blo
     """Slot resolution and the write in one launch (see include/pagedkv.h).  The resolved
     slots go to `slot_mapping` (int64 [num_tokens]) when one is given, which is returned."""
     lib = load_library()
+    _debug("paged_kv_write_positions", "paged_kv_check_positions", seq_ids, positions, block_tables, k_cache,
+           kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
     assert seq_ids.dtype == torch.int32 and positions.dtype == torch.int32
     assert block_tables.dtype == torch.int32 and seq_ids.numel() == positions.numel()
@@ -259,6 +274,8 @@ def paged_attention_prefill(q: torch.Tensor, cu_q: torch.Tensor, max_q_len: int,
     """Chunked-prefill attention into `out` ([rows][H_q][D]); see include/pagedkv.h.
     kv_dtype / k_scale / v_scale describe an fp8 cache as for paged_attention_decode."""
     lib = load_library()
+    _debug("paged_attention_prefill", "paged_attention_check_prefill", cu_q, max_q_len, block_tables,
+           context_lens, max_context_len, k_cache, kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
     rows, hq, d = q.shape
     assert cu_q.dtype == torch.int32 and block_tables.dtype == torch.int32
@@ -277,6 +294,8 @@ def paged_kv_copy_blocks(src_ids: torch.Tensor, dst_ids: torch.Tensor, k_cache: 
                          v_cache: torch.Tensor, kv_dtype=None, stream=None) -> None:
     """Copy-on-write: block src_ids[i] -> dst_ids[i] in both caches (int32 device IDs)."""
     lib = load_library()
+    _debug("paged_kv_copy_blocks", "paged_kv_check_block_ids", src_ids, dst_ids, k_cache, kv_dtype=kv_dtype,
+           stream=stream)
     desc = cache_desc(k_cache, kv_dtype)
     assert src_ids.dtype == torch.int32 and dst_ids.dtype == torch.int32 and src_ids.numel() == dst_ids.numel()
     _check("paged_kv_copy_blocks",
@@ -300,6 +319,7 @@ def paged_kv_swap_in(ids: torch.Tensor, k_buf: torch.Tensor, v_buf: torch.Tensor
                      v_cache: torch.Tensor, kv_dtype=None, stream=None) -> None:
     """Row i of the buffers (device or pinned host tensors) -> blocks ids[i] of each cache."""
     lib = load_library()
+    _debug("paged_kv_swap_in", "paged_kv_check_block_ids", None, ids, k_cache, kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype)
     assert ids.dtype == torch.int32
     _check("paged_kv_swap_in",
@@ -395,6 +415,8 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     them zero) is allocated here by torch when the call needs one and none is given.
     shared_blocks: see cache_desc."""
     lib = load_library()
+    _debug("paged_attention_decode", "paged_attention_check_decode", block_tables, context_lens, max_context_len,
+           k_cache, kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale, shared_blocks)
     n, hq, d = q.shape
     qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
@@ -425,6 +447,8 @@ def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cac
     library's per-GPU scratch array serves instead (see include/pagedkv.h; calls that
     overlap on one GPU race)."""
     lib = load_library()
+    _debug("paged_attention_decode_noalloc", "paged_attention_check_decode", block_tables, context_lens,
+           max_context_len, k_cache, kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale, shared_blocks)
     n, hq, d = q.shape
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
@@ -449,6 +473,8 @@ def paged_attention_decode_window(q: torch.Tensor, k_cache: torch.Tensor, v_cach
     """Decode attention into `out` over the last `window` tokens of each context plus its
     first `sinks` (window 0: every token).  Other arguments as paged_attention_decode."""
     lib = load_library()
+    _debug("paged_attention_decode_window", "paged_attention_check_decode", block_tables, context_lens,
+           max_context_len, k_cache, window=window, sinks=sinks, kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale, shared_blocks)
     n, hq, d = q.shape
     qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
@@ -491,6 +517,9 @@ def paged_attention_decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor,
     (zero-headed, as for paged_attention_decode) is allocated by torch when not given.
     kv_dtype / k_scale / v_scale describe an fp8 cache as for paged_attention_decode."""
     lib = load_library()
+    _debug("paged_attention_decode_shared_prefix", "paged_attention_check_shared_prefix", block_tables,
+           context_lens, max_context_len, group_starts, prefix_lens, max_group_size, max_prefix_len, k_cache,
+           kv_dtype=kv_dtype, stream=stream)
     desc = cache_desc(k_cache, kv_dtype, k_scale, v_scale)
     n, hq, d = q.shape
     qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)

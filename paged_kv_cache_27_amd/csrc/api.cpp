@@ -371,7 +371,7 @@ int scratch_for_current_device(hipStream_t stream, void** out) {
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 8; }
+int32_t pkv_abi_version(void) { return 9; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -474,6 +474,164 @@ int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const v
     return PKV_ERR_SHAPE;
   hipError_t e = pkv::launch_move_blocks(kd, vd, nullptr, k_cache, v_cache, ids, num,
                                          block_bytes(cache), cache->num_blocks, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+// ---- input checks ------------------------------------------------------------------
+// The result must be device memory the kernels can update with device-scope atomics: a
+// NULL or misaligned pointer, or one the runtime does not know as device memory, is
+// refused before anything is launched.
+static int check_result_ptr(pkv_check_result* result) {
+  if (!result) return PKV_ERR_NULL;
+  if ((uintptr_t)result & 7u) return PKV_ERR_SHAPE;
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, result) != hipSuccess) {
+    (void)hipGetLastError();
+    return PKV_ERR_SHAPE;
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+// Host-side checks shared by the attention checks: the sizes a call of that kind refuses.
+static int check_attention_sizes(int32_t num_seqs, const pkv_cache_desc* cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * cache->block_size < max_context_len) return PKV_ERR_SHAPE;
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return PKV_ERR_NULL;
+  return PKV_OK;
+}
+
+static pkv::SeqCheckArgs seq_check_args(int32_t num_seqs, const pkv_cache_desc* cache, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                        int32_t max_context_len) {
+  pkv::SeqCheckArgs a = {};
+  a.num_seqs = num_seqs;
+  a.num_blocks = cache->num_blocks;
+  a.block_size = cache->block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  return a;
+}
+
+int paged_kv_check_slots(const int64_t* slot_mapping, int32_t num_tokens, const pkv_cache_desc* cache,
+                         pkv_check_result* result, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens > 0 && !slot_mapping) return PKV_ERR_NULL;
+  if ((st = check_result_ptr(result))) return st;
+  pkv::DupCheckArgs a = {};
+  a.n = num_tokens;
+  a.rows = cache->num_blocks * cache->block_size;
+  a.slots = slot_mapping;
+  hipError_t e = pkv::launch_check_dups(pkv::kDupSlots, a, result, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_kv_check_positions(const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                             int32_t num_seqs, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const pkv_cache_desc* cache, pkv_check_result* result, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if (num_tokens > 0 && (!seq_ids || !positions || (num_seqs > 0 && !block_tables))) return PKV_ERR_NULL;
+  if ((st = check_result_ptr(result))) return st;
+  pkv::DupCheckArgs a = {};
+  a.n = num_tokens;
+  a.rows = cache->num_blocks * cache->block_size;
+  a.seq_ids = seq_ids;
+  a.positions = positions;
+  a.num_seqs = num_seqs;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = cache->block_size;
+  hipError_t e = pkv::launch_check_dups(pkv::kDupPositions, a, result, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_check_decode(int32_t num_seqs, const pkv_cache_desc* cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, int32_t window, int32_t sinks,
+                                 pkv_check_result* result, hipStream_t stream) {
+  int st = check_attention_sizes(num_seqs, cache, block_tables, max_blocks_per_seq, context_lens, max_context_len);
+  if (st) return st;
+  if (window < 0 || sinks < 0) return PKV_ERR_SHAPE;
+  if ((st = check_result_ptr(result))) return st;
+  pkv::SeqCheckArgs a = seq_check_args(num_seqs, cache, block_tables, max_blocks_per_seq, context_lens,
+                                       max_context_len);
+  a.window = window;
+  a.sinks = sinks;
+  hipError_t e = pkv::launch_check_seqs(a, nullptr, result, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_check_shared_prefix(int32_t num_seqs, const pkv_cache_desc* cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        const int32_t* group_starts, int32_t num_groups,
+                                        int32_t max_group_size, const int32_t* prefix_lens,
+                                        int32_t max_prefix_len, pkv_check_result* result,
+                                        hipStream_t stream) {
+  int st = check_attention_sizes(num_seqs, cache, block_tables, max_blocks_per_seq, context_lens, max_context_len);
+  if (st) return st;
+  if (num_seqs > 0) {
+    if (num_groups < 1 || num_groups > num_seqs || max_group_size < 1 || max_prefix_len < 0) return PKV_ERR_SHAPE;
+    if (max_prefix_len % cache->block_size != 0 || max_prefix_len > max_context_len) return PKV_ERR_SHAPE;
+    if (!group_starts || !prefix_lens) return PKV_ERR_NULL;
+  }
+  if ((st = check_result_ptr(result))) return st;
+  pkv::SeqCheckArgs a = seq_check_args(num_seqs, cache, block_tables, max_blocks_per_seq, context_lens,
+                                       max_context_len);
+  pkv::GroupCheckArgs g = {};
+  g.num_seqs = num_seqs;
+  g.num_groups = num_groups;
+  g.max_group_size = max_group_size;
+  g.max_prefix_len = max_prefix_len;
+  g.block_size = cache->block_size;
+  g.max_blocks_per_seq = max_blocks_per_seq;
+  g.group_starts = group_starts;
+  g.prefix_lens = prefix_lens;
+  g.context_lens = context_lens;
+  g.block_tables = block_tables;
+  hipError_t e = pkv::launch_check_seqs(a, &g, result, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_check_prefill(int32_t num_seqs, const int32_t* cu_q, int32_t max_q_len,
+                                  const pkv_cache_desc* cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, pkv_check_result* result, hipStream_t stream) {
+  int st = check_attention_sizes(num_seqs, cache, block_tables, max_blocks_per_seq, context_lens, max_context_len);
+  if (st) return st;
+  if (max_q_len < 0 || max_q_len > max_context_len) return PKV_ERR_SHAPE;
+  if (num_seqs > 0 && !cu_q) return PKV_ERR_NULL;
+  if ((st = check_result_ptr(result))) return st;
+  pkv::SeqCheckArgs a = seq_check_args(num_seqs, cache, block_tables, max_blocks_per_seq, context_lens,
+                                       max_context_len);
+  a.cu_q = cu_q;
+  a.max_q_len = max_q_len;
+  hipError_t e = pkv::launch_check_seqs(a, nullptr, result, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_kv_check_block_ids(const int32_t* src_ids, const int32_t* dst_ids, int32_t num,
+                             const pkv_cache_desc* cache, pkv_check_result* result, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (num < 0) return PKV_ERR_SHAPE;
+  if (num > 0 && !dst_ids) return PKV_ERR_NULL;
+  if ((st = check_result_ptr(result))) return st;
+  pkv::DupCheckArgs a = {};
+  a.n = num;
+  a.rows = cache->num_blocks;
+  a.src_ids = src_ids;
+  a.dst_ids = dst_ids;
+  hipError_t e = pkv::launch_check_dups(pkv::kDupBlocks, a, result, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -136,4 +136,40 @@ inline size_t ws_total_bytes(int64_t n, int64_t hq, int64_t d, int64_t parts) {
          align256((size_t)(n * hq * parts * d) * sizeof(float));
 }
 
+// ---- input checks (check.hip); `result` is the caller's pkv_check_result ----
+struct SeqCheckArgs {
+  int64_t num_seqs;
+  int64_t num_blocks;
+  int32_t block_size, max_blocks_per_seq, max_context_len;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t window, sinks;  // decode over a window (window 0: every token)
+  const int32_t* cu_q;    // prefill: query rows [num_seqs + 1]; null otherwise
+  int32_t max_q_len;
+};
+struct GroupCheckArgs {  // shared-prefix grouping
+  int32_t num_seqs, num_groups, max_group_size, max_prefix_len, block_size, max_blocks_per_seq;
+  const int32_t* group_starts;
+  const int32_t* prefix_lens;
+  const int32_t* context_lens;
+  const int32_t* block_tables;
+};
+enum DupMode { kDupSlots = 0, kDupPositions = 1, kDupBlocks = 2 };
+struct DupCheckArgs {
+  int64_t n;     // entries
+  int64_t rows;  // slots: num_blocks * block_size; block pairs: num_blocks
+  const int64_t* slots;
+  const int32_t* seq_ids;
+  const int32_t* positions;
+  int32_t num_seqs, max_blocks_per_seq, block_size;
+  const int32_t* block_tables;
+  const int32_t* src_ids;  // block pairs: null for swap in
+  const int32_t* dst_ids;
+};
+// CONTEXT_LEN / QUERY_ROWS / BLOCK_ID per sequence, and with `groups` the shared-prefix
+// rules; a clear, the checks and the final write of `result`, in order on `stream`.
+hipError_t launch_check_seqs(const SeqCheckArgs& a, const GroupCheckArgs* groups, void* result,
+                             hipStream_t stream);
+hipError_t launch_check_dups(int mode, const DupCheckArgs& a, void* result, hipStream_t stream);
+
 }  // namespace pkv

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pkv.pkv_abi_version() == 8
+    assert pkv.pkv_abi_version() == 9
 
 
 def test_cache_desc_mirror_matches_the_c_layout(tmp_path):
@@ -322,3 +322,58 @@ def test_probe_library_argument_errors():
     assert f(FAKE, FAKE, FAKE, 5, 4096, None, None) == -1
     assert f(FAKE, FAKE, FAKE, 5, 3000, FAKE, None) == -3  # unsupported tile size
     assert f(ctypes.c_void_p(0x100004), FAKE, FAKE, 5, 4096, FAKE, None) == -3
+
+
+def test_input_check_argument_errors():
+    """The input checks refuse bad sizes, NULL arrays, and a NULL, misaligned or non-device
+    result before launching anything."""
+    from paged_kv_cache_27_amd._checks import _lib
+    lib = _lib()
+    d = ctypes.byref(_desc())  # blocks of 16 tokens
+    host_words = (ctypes.c_int64 * 3)()
+    host = ctypes.cast(host_words, ctypes.c_void_p)  # host memory: refused as the result
+    mis = ctypes.c_void_p(0x100004)
+    slots, pos = lib.paged_kv_check_slots, lib.paged_kv_check_positions
+    dec, pre = lib.paged_attention_check_decode, lib.paged_attention_check_shared_prefix
+    pf, blk = lib.paged_attention_check_prefill, lib.paged_kv_check_block_ids
+    # slots (slot_mapping, n, desc, result, stream)
+    assert slots(FAKE, -1, d, FAKE, None) == -3
+    assert slots(None, 4, d, FAKE, None) == -1
+    assert slots(FAKE, 4, None, FAKE, None) == -1
+    assert slots(FAKE, 4, d, None, None) == -1
+    assert slots(FAKE, 4, d, mis, None) == -3
+    assert slots(FAKE, 4, d, host, None) == -3
+    assert slots(FAKE, 4, ctypes.byref(_desc(block_size=8)), FAKE, None) == -3
+    # positions (seq_ids, positions, n, num_seqs, tables, max_blocks, desc, result, stream)
+    assert pos(FAKE, FAKE, -1, 2, FAKE, 4, d, FAKE, None) == -3
+    assert pos(FAKE, FAKE, 3, -1, FAKE, 4, d, FAKE, None) == -3
+    assert pos(FAKE, FAKE, 3, 2, FAKE, 0, d, FAKE, None) == -3
+    assert pos(None, FAKE, 3, 2, FAKE, 4, d, FAKE, None) == -1
+    assert pos(FAKE, FAKE, 3, 2, None, 4, d, FAKE, None) == -1
+    assert pos(FAKE, FAKE, 3, 0, None, 4, d, host, None) == -3  # no sequence: no table needed
+    # decode (n, desc, tables, max_blocks, context_lens, max_context_len, window, sinks, result, stream)
+    assert dec(-1, d, FAKE, 4, FAKE, 64, 0, 0, FAKE, None) == -3
+    assert dec(2, d, FAKE, 4, FAKE, 65, 0, 0, FAKE, None) == -3  # a row of 4 blocks holds 64 tokens
+    assert dec(2, d, FAKE, 4, FAKE, 64, -1, 0, FAKE, None) == -3
+    assert dec(2, d, FAKE, 4, FAKE, 64, 8, -2, FAKE, None) == -3
+    assert dec(2, d, None, 4, FAKE, 64, 0, 0, FAKE, None) == -1
+    assert dec(2, d, FAKE, 4, FAKE, 64, 0, 0, None, None) == -1
+    assert dec(2, d, FAKE, 4, FAKE, 64, 0, 0, host, None) == -3
+    # shared prefix (n, desc, tables, max_blocks, context_lens, max_context_len, group_starts,
+    # num_groups, max_group_size, prefix_lens, max_prefix_len, result, stream)
+    ok = [4, d, FAKE, 4, FAKE, 64, FAKE, 2, 2, FAKE, 32]
+    assert pre(*ok, host, None) == -3
+    for k, v, want in ((7, 0, -3), (7, 5, -3), (8, 0, -3), (10, 40, -3), (10, -16, -3), (10, 80, -3),
+                       (6, None, -1), (9, None, -1)):
+        args = list(ok)
+        args[k] = v
+        assert pre(*args, FAKE, None) == want, (k, v)
+    # prefill (n, cu_q, max_q_len, desc, tables, max_blocks, context_lens, max_context_len, result, stream)
+    assert pf(2, FAKE, -1, d, FAKE, 4, FAKE, 64, FAKE, None) == -3
+    assert pf(2, FAKE, 65, d, FAKE, 4, FAKE, 64, FAKE, None) == -3
+    assert pf(2, None, 8, d, FAKE, 4, FAKE, 64, FAKE, None) == -1
+    assert pf(2, FAKE, 8, d, FAKE, 4, FAKE, 64, host, None) == -3
+    # block IDs (src_ids, dst_ids, n, desc, result, stream)
+    assert blk(FAKE, FAKE, -1, d, FAKE, None) == -3
+    assert blk(FAKE, None, 3, d, FAKE, None) == -1
+    assert blk(None, FAKE, 3, d, host, None) == -3
