@@ -144,6 +144,13 @@ __global__ void __launch_bounds__(64 * kRowsWaves)
 rows_kernel(const RowsArgs a) {
   using O_ = PfxOps<QT>;
   using frag8 = typename O_::frag8;
+  // P.V over an fp8 cache runs on the f16 MFMA with one f16 P (rounded toward zero,
+  // < 2^-10 relative): its V codes convert to f16 exactly, and the fp8 tolerance leaves
+  // room for that rounding.  Over 16-bit caches P keeps ~16 bits (hi + lo, two MFMAs):
+  // a bf16 output's own rounding leaves too little of the tolerance for more.
+  constexpr bool SINGLE_P = KV == kFP8;
+  using PV_ = PfxOps<SINGLE_P ? kF16 : QT>;
+  using pfrag8 = typename PV_::frag8;
   constexpr int EB = KV == kFP8 ? 1 : 2;  // cache element bytes
   constexpr int ROW = EB * D;          // bytes of one cache K/V row
   constexpr int QROW = 2 * D;          // bytes of one query row
@@ -363,7 +370,7 @@ rows_kernel(const RowsArgs a) {
         uint32_t x0[8], x1[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint2 c = O_::from_fp8(w[e]);
+          const uint2 c = PV_::from_fp8(w[e]);  // V in the P.V type
           x0[e] = c.x;
           x1[e] = c.y;
         }
@@ -445,7 +452,7 @@ rows_kernel(const RowsArgs a) {
         }
       }
     }
-    frag8 ahi[RS], alo[RS];
+    pfrag8 ahi[RS], alo[RS];
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
       float p[8];
@@ -453,25 +460,30 @@ rows_kernel(const RowsArgs a) {
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[rs][i], c_l2, -m[rs]));
       uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O_::split2(p[2 * i], p[2 * i + 1], hw[i], lw[i]);
-      ahi[rs] = __builtin_bit_cast(frag8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      alo[rs] = __builtin_bit_cast(frag8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (SINGLE_P)
+          hw[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p[2 * i], p[2 * i + 1]));
+        else
+          PV_::split2(p[2 * i], p[2 * i + 1], hw[i], lw[i]);
+      }
+      ahi[rs] = __builtin_bit_cast(pfrag8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      if constexpr (!SINGLE_P) alo[rs] = __builtin_bit_cast(pfrag8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       if constexpr (VSUM) {
         lrow[rs] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       } else {
-        const frag8 ones = __builtin_bit_cast(frag8, make_uint4(O_::kOne, O_::kOne, O_::kOne, O_::kOne));
-        Om[rs] = O_::qk(ahi[rs], ones, Om[rs]);
-        Om[rs] = O_::qk(alo[rs], ones, Om[rs]);
+        const pfrag8 ones = __builtin_bit_cast(pfrag8, make_uint4(PV_::kOne, PV_::kOne, PV_::kOne, PV_::kOne));
+        Om[rs] = PV_::qk(ahi[rs], ones, Om[rs]);
+        if constexpr (!SINGLE_P) Om[rs] = PV_::qk(alo[rs], ones, Om[rs]);
       }
     }
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
-      const frag8 vf = __builtin_bit_cast(
-          frag8, *(const uint4*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 8]);
+      const pfrag8 vf = __builtin_bit_cast(
+          pfrag8, *(const uint4*)&lds_v[buf][((lane >> 4) * D + 16 * jj + (lane & 15)) * 8]);
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs) {
-        O[rs][jj] = O_::qk(ahi[rs], vf, O[rs][jj]);
-        O[rs][jj] = O_::qk(alo[rs], vf, O[rs][jj]);
+        O[rs][jj] = PV_::qk(ahi[rs], vf, O[rs][jj]);
+        if constexpr (!SINGLE_P) O[rs][jj] = PV_::qk(alo[rs], vf, O[rs][jj]);
       }
     }
   };
