@@ -367,9 +367,10 @@ int paged_kv_swap_in(const int32_t* ids, int32_t num, const void* k_buf, const v
  * device (a call that breaks one reads or writes memory the caller did not mean, or
  * races).  Each check reads only the index arrays it is given -- never a cache -- within
  * the bounds its size arguments give, and reports into `result`, a pkv_check_result in
- * device memory (8-byte aligned) that the check initialises itself: three kernels in
- * order on `stream`, no memset, no allocation, no synchronisation, so `result` is valid
- * once the stream has passed the call.  Host-visible argument errors return before
+ * device memory (8-byte aligned) that the check initialises itself: a clearing kernel,
+ * the check's kernels and a final kernel, in order on `stream`, with no memset, no
+ * allocation and no synchronisation, so `result` is valid once the stream has passed the
+ * call.  Host-visible argument errors return before
  * anything is launched: PKV_ERR_NULL for a NULL result or a NULL array the check reads,
  * PKV_ERR_SHAPE for negative sizes, the bounds the checked call refuses (a table row
  * shorter than max_context_len, max_q_len above it, the shared-prefix bounds), or a

@@ -1,7 +1,8 @@
 // Input checks for gfx950: the preconditions the hot-path calls leave unchecked on the
-// device, tested on the caller's index arrays alone (never a cache).  Each check is three
-// launches in order on one stream: clear the result, test the entries, turn the result's
-// accumulators into the reported form.
+// device, tested on the caller's index arrays alone (never a cache).  Each check runs in
+// order on one stream: a launch that clears the result, the launches that test the entries
+// (one, or three for the shared-prefix rules), and one that turns the result's accumulators
+// into the reported form.
 //
 // The rules follow from what the calls do with their indices:
 //   * a slot names one cache row, block_tables[s][p / B] * B + p % B ("Optimizacion de
