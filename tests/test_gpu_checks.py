@@ -251,3 +251,30 @@ def test_debug_mode_shared_prefix_and_prefill(monkeypatch):
     assert e.value.result.code == 8
     torch.cuda.synchronize()
     assert torch.isnan(rows.float()).all()
+
+
+def test_duplicate_checks_at_prefill_scale():
+    """The pairwise duplicate rules on 40 000 entries (a long prefill chunk's slots, a large
+    copy-on-write batch): exact against the oracle, and quick enough for a debugging aid."""
+    import time
+    rng = np.random.default_rng(4242)
+    nb, B, n = 4096, 16, 40000
+    kc = _cache(nb, B)
+    slots = rng.permutation(nb * B)[:n].astype(np.int64)
+    slots[[123, 39000]] = slots[[7, 20000]]  # two duplicates, of earlier entries
+    dev = _dev(slots, np.int64)
+    pkv.paged_kv_check_slots(dev, kc)  # warm
+    t = time.perf_counter()
+    got = tuple(pkv.paged_kv_check_slots(dev, kc))
+    ms = (time.perf_counter() - t) * 1e3
+    print(f"slot check over {n} tokens: {ms:.1f} ms", flush=True)
+    assert got == C.check_slots(slots, nb, B) == (2, C.DUPLICATE_SLOT, 123)
+    assert ms < 1000
+    dst = rng.permutation(nb)[: nb // 2].astype(np.int32)
+    src = rng.permutation(nb)[: nb // 2].astype(np.int32)
+    src = np.where(np.isin(src, dst), -1, src).astype(np.int32)  # sources never destinations ...
+    src[5] = dst[900]  # ... but one
+    dst = np.tile(dst, 20)[:n]
+    src = np.tile(src, 20)[:n]
+    got = tuple(pkv.paged_kv_check_block_ids(_dev(src), _dev(dst), kc))
+    assert got == C.check_block_ids(src, dst, nb), got
