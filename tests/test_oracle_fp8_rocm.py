@@ -1,0 +1,71 @@
+"""The oracle's fp8 encoder against an independent implementation: ROCm's software
+conversion of fp32 to OCP e4m3fn (hip/hip_fp8.h, host path) in its saturate-to-finite
+mode, built from tests/golden/fp8_rocm_reference.cpp and run on the host (no GPU).
+
+* every finite input: the same code -- values within +-448 rounded to nearest even (a
+  second reference beside torch's cast), and finite values beyond +-448 saturated to
+  +-448, the part of reading R8 that torch's cast (NaN there) cannot pin;
+* NaN stays NaN on both sides;
+* +-infinity: ROCm's conversion gives NaN, while R8 saturates infinities to +-448 as it
+  does every other value past the largest finite one.  The pages do not say which; R8's
+  choice stays (a cache holds finite values either way), and this difference is asserted
+  as it stands so that a change on either side shows.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+SRC = Path(__file__).resolve().parent / "golden" / "fp8_rocm_reference.cpp"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+@pytest.fixture(scope="module")
+def rocm_encode():
+    if not (Path(HIPCC).exists() or shutil.which(HIPCC)):
+        pytest.skip("hipcc is not installed")
+    tmp = Path(tempfile.mkdtemp(prefix="fp8ref"))
+    exe = tmp / "fp8ref"
+    r = subprocess.run([HIPCC, "-x", "hip", "--offload-host-only", "-O1", str(SRC), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip(f"the ROCm fp8 header could not be built on the host: {r.stderr[-300:]}")
+
+    def encode(x: np.ndarray) -> np.ndarray:
+        bits = np.asarray(x, np.float32).view(np.uint32)
+        out = subprocess.run([str(exe)], input="\n".join(f"{b:08x}" for b in bits) + "\n",
+                             capture_output=True, text=True, check=True).stdout.split()
+        return np.array([int(c, 16) for c in out], np.uint8)
+
+    yield encode
+    shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_finite_values_match_rocm(orc, rocm_encode):
+    rng = np.random.default_rng(8)
+    x = np.concatenate([
+        rng.normal(0, 1, 3000), rng.normal(0, 100, 3000), rng.uniform(-448, 448, 3000),
+        rng.normal(0, 1e-2, 1000), rng.normal(0, 1e-3, 1000),            # subnormal codes
+        np.ldexp(1.0, np.arange(-12, 9)), -np.ldexp(1.0, np.arange(-12, 9)),
+        np.arange(0, 449, 0.5),                                          # ties among them
+        [448, 449, 463.99, 464, 464.01, 479, 480, 481, 500, 1e4, 1e6, 3.4e38],  # past +-448
+        [-448, -449, -464, -480, -1e6, -3.4e38], [0.0, -0.0],
+    ]).astype(np.float32)
+    want = rocm_encode(x)
+    got = orc.f32_to_fp8(x)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(want[i])) for i in bad[:10]]
+    assert set(want[x >= 448].tolist()) == {0x7E} and set(want[x <= -448].tolist()) == {0xFE}
+
+
+def test_nan_and_infinities(orc, rocm_encode):
+    x = np.array([np.nan, np.inf, -np.inf], np.float32)
+    want = rocm_encode(x)
+    got = orc.f32_to_fp8(x)
+    assert want[0] & 0x7F == 0x7F and got[0] & 0x7F == 0x7F         # NaN stays NaN
+    assert want[1:].tolist() == [0x7F, 0xFF]                           # ROCm: infinity -> NaN
+    assert got[1:].tolist() == [0x7E, 0xFE]                            # R8: infinity -> +-448
