@@ -1,6 +1,6 @@
 """The oracle's fp8 encoder against an independent implementation: ROCm's software
 conversion of fp32 to OCP e4m3fn (hip/hip_fp8.h, host path) in its saturate-to-finite
-mode, built from tests/golden/fp8_rocm_reference.cpp and run on the host (no GPU).
+mode, built from tests/fp8_rocm_reference.cpp and run on the host (no GPU).
 
 * every finite input: the same code -- values within +-448 rounded to nearest even (a
   second reference beside torch's cast), and finite values beyond +-448 saturated to
@@ -20,7 +20,7 @@ from pathlib import Path
 import numpy as np
 import pytest
 
-SRC = Path(__file__).resolve().parent / "golden" / "fp8_rocm_reference.cpp"
+SRC = Path(__file__).resolve().parent / "fp8_rocm_reference.cpp"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
