@@ -16,7 +16,9 @@ and the same calls run eagerly with their own output and workspace; then:
   * the workspace's counter header is zero again after the replay;
   * the first replay, on the workload's own inputs, is within the decode bar of the oracle.
 Between replays only eager work and synchronisations run; nothing in the graphs clears
-memory with a memset.
+memory with a memset.  A last case captures an input check (through the C ABI, which
+neither waits nor allocates) and plants different out-of-range block IDs before each
+replay: every replay reports the tables as they are then, exactly as the oracle's rules.
 """
 import os
 
@@ -236,3 +238,44 @@ def test_graph_noalloc_step(orc):
     first = _replay_and_compare(step, "no-alloc", warm=False)
     _, _, _, ref = oracle_step(orc, step.w, threads=THREADS)
     assert_close_to_oracle(first, ref, cfg.kv_dtype, "graph case no-alloc")
+
+
+def test_graph_input_check_replays():
+    """An input check captured through the C ABI (no memset, no synchronisation, it clears
+    its own result): each replay reports the tables as they are at that replay."""
+    import ctypes
+    from oracle import checks as C
+    from paged_kv_cache_27_amd._checks import _lib, RESULT_BYTES
+    w = make_workload(LLAMA8B.replace(num_seqs=16, num_q_heads=8, num_kv_heads=2, ctx_params=(100, 2500),
+                                      seed=39))
+    g = GpuStep(w)
+    desc = pkv.cache_desc(g.k_cache)
+    bt = g.block_tables.clone()
+    res = torch.zeros(RESULT_BYTES, dtype=torch.uint8, device="cuda")
+    lib = _lib()
+    pkv.paged_attention_check_decode(bt, g.context_lens, w.max_context_len, g.k_cache)  # set-up outside capture
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st = lib.paged_attention_check_decode(w.cfg.num_seqs,
+                                              ctypes.byref(desc), bt.data_ptr(), bt.shape[1],
+                                              g.context_lens.data_ptr(), w.max_context_len, 0, 0, res.data_ptr(),
+                                              torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    rng = np.random.default_rng(40)
+    for r in range(4):
+        table = w.block_tables.copy()
+        for _ in range(r):  # r planted out-of-range IDs among the entries the decode reads
+            s = int(rng.integers(w.cfg.num_seqs))
+            table[s, int(rng.integers(-(-int(w.context_lens[s]) // w.cfg.block_size)))] = w.num_blocks + r
+        bt.copy_(torch.from_numpy(table))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        raw = res.cpu().numpy()
+        got = (int(raw[16:24].view(np.int64)[0]), int(raw[0:4].view(np.int32)[0]), int(raw[8:16].view(np.int64)[0]))
+        want = C.check_decode(table, w.context_lens, w.max_context_len, w.num_blocks, w.cfg.block_size)
+        print(f"graph case input check: replay {r}: {got}", flush=True)
+        assert got == want, (r, got, want)
+        eager = pkv.paged_attention_check_decode(bt, g.context_lens, w.max_context_len, g.k_cache)
+        assert tuple(eager) == want
+    del graph
